@@ -1,0 +1,131 @@
+/*
+ * attn_prefix.h -- C ABI of the prefix-masked / split-KV attention library
+ * (libattnprefix.so, HIP kernels for gfx950 / MI355X).
+ *
+ * The operation.  Each batch element b has a key-padding mask whose valid keys
+ * are exactly the first n_b = kv_len[b] rows.  Masking the other keys is the
+ * same as cutting k and v down to their first n_b rows and attending with no
+ * mask at all (page "Rewrite prefix key-padding masks as k/v truncation to keep
+ * SDPA on the flash path (PyTorch)", tabfm PR #80, section Fix; a ragged mask,
+ * one n_b per element, equals per-element truncated forwards, section Tests).
+ * A prefix mask is therefore carried as one length per batch element instead
+ * of a dense mask (page "Add sequence-parallel multi-GPU inference (PyTorch and
+ * JAX) and a cuDNN flash attention option", tabfm PR #81, section cuDNN flash
+ * attention).  For every (b, h, query row i):
+ *
+ *     out[b,h,i,:] = sum_{j < n_b} softmax_j(scale * q_i . k_j) * v_j
+ *     lse[b,h,i]   = ln sum_{j < n_b} exp(scale * q_i . k_j)       (natural log)
+ *
+ * and n_b = 0 gives out = 0, lse = -inf.  The kernels read only the first n_b
+ * key rows (padded slots cost no bandwidth and their contents, even NaN, never
+ * reach a result), keep the softmax in fp32 and never form the [T_q, n] score
+ * matrix.  The split-KV form computes normalized partials over fixed key
+ * chunks and merges them exactly with log-sum-exp weights (PR #81, section
+ * Sequence-parallel inference).
+ *
+ * Layout.  Row-major, D fastest, no strides:
+ *     q, out     [B, H, Tq, D]
+ *     k, v       [B, H, S, D]      S = allocated key slots, 0 <= n_b <= S
+ *     lse        [B, H, Tq]        fp32
+ *     part_out   [B, H, C, Tq, D]  fp32, C = attn_splitkv_num_chunks(S, chunk)
+ *     part_lse   [B, H, C, Tq]     fp32
+ *     kv_len     [B]               int32
+ *
+ * Pointers.  Every tensor pointer is a DEVICE pointer (HIP memory of the
+ * current device); `stream` is a hipStream_t passed as void* (NULL = the null
+ * stream).  Calls only enqueue work on `stream` and return; buffers must stay
+ * alive until that work completes.  The caller owns every buffer: the library
+ * allocates no memory, keeps no pointer after a call returns and holds no
+ * mutable global state, so calls are re-entrant.
+ *
+ * Errors.  Every call validates its arguments on the host BEFORE any HIP call
+ * and returns a status code; no call ever falls back to another algorithm.
+ * kv_len values live on the device and cannot be checked without a sync: the
+ * kernels clamp n_b into [0, S] (so memory stays safe), and values outside
+ * that range are a caller error with unspecified results.  A failed launch
+ * returns ATTN_ERR_HIP.
+ *
+ * Limits.  D in {64, 128, 256}; dtype bf16 or fp32 (inputs and `out` share
+ * it); S * D * sizeof(dtype) < 2^31 per (b, h); the number of workgroups
+ * (B * H * ceil(Tq / 128) [* C]) below 2^31.  Zero B, H or Tq is a no-op
+ * returning ATTN_OK (then the tensor pointers may be NULL); S = 0 is legal
+ * (every n_b is 0) and then k and v may be NULL.
+ */
+#ifndef ATTN_PREFIX_H
+#define ATTN_PREFIX_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  ATTN_OK = 0,
+  ATTN_ERR_NULLPTR = 1,      /* a required pointer is NULL */
+  ATTN_ERR_SHAPE = 2,        /* a negative size, or a size beyond the limits above */
+  ATTN_ERR_DTYPE = 3,        /* dtype is not one of attn_dtype_t */
+  ATTN_ERR_UNSUPPORTED = 4,  /* head dim D not in {64, 128, 256} */
+  ATTN_ERR_ALIGN = 5,        /* a tensor pointer is not 16-byte aligned */
+  ATTN_ERR_CHUNK = 6,        /* chunk <= 0 or not a multiple of 64 */
+  ATTN_ERR_HIP = 7,          /* the HIP runtime reported an error at launch */
+  ATTN_ERR_ARG = 8           /* a scalar argument is out of range (e.g. non-finite scale) */
+} attn_status_t;
+
+typedef enum { ATTN_BF16 = 0, ATTN_F32 = 1 } attn_dtype_t;
+
+/* Library version as (major << 16) | (minor << 8) | patch. */
+int attn_version(void);
+
+/* Fused prefix-masked attention forward.
+ * Defined by the truncation identity of tabfm PR #80 (section Fix) and the
+ * per-element (ragged) form of its section Tests; kv_len plays the role of the
+ * sequence lengths of PR #81 (section cuDNN flash attention).
+ *   q, k, v  : device, dtype, layouts above (k, v: only rows j < n_b are read)
+ *   kv_len   : device int32 [B]
+ *   scale    : softmax scale (e.g. 1/sqrt(D)); must be finite
+ *   out      : device, dtype, [B,H,Tq,D]; every element is written
+ *   lse      : device fp32 [B,H,Tq] natural-log LSE, or NULL to skip it
+ */
+attn_status_t attn_prefix_fwd(const void* q, const void* k, const void* v, const int32_t* kv_len,
+                              int B, int H, int Tq, int S, int D, float scale, attn_dtype_t dtype,
+                              void* out, float* lse, void* stream);
+
+/* Split-KV partials: for chunk c the keys [c*chunk, min((c+1)*chunk, n_b)).
+ * Each partial is the normalized output O_c (fp32) with its natural-log LSE
+ * L_c over that chunk's keys; an empty chunk writes O_c = 0, L_c = -inf.
+ * This is one device's share of the inducing attention of tabfm PR #81
+ * (section Sequence-parallel inference), cut at fixed key boundaries.
+ *   chunk    : keys per chunk, a positive multiple of 64; C = ceil(S / chunk)
+ *   part_out : device fp32 [B,H,C,Tq,D], fully written
+ *   part_lse : device fp32 [B,H,C,Tq], fully written
+ */
+attn_status_t attn_splitkv_partial(const void* q, const void* k, const void* v, const int32_t* kv_len,
+                                   int B, int H, int Tq, int S, int D, float scale, attn_dtype_t dtype,
+                                   int chunk, float* part_out, float* part_lse, void* stream);
+
+/* Exact log-sum-exp merge of C partials (tabfm PR #81, section
+ * Sequence-parallel inference): with M = max_c L_c,
+ *     M = -inf  ->  out = 0, lse = -inf
+ *     else      ->  w_c = exp(L_c - M), out = sum_c w_c O_c / sum_c w_c,
+ *                   lse = M + ln sum_c w_c.
+ * Any partition works (chunks of any size, empty ones included).
+ *   part_out : device fp32 [B,H,C,Tq,D]; part_lse: device fp32 [B,H,C,Tq]
+ *   out      : device, out_dtype, [B,H,Tq,D]
+ *   lse      : device fp32 [B,H,Tq], or NULL
+ * C = 0 is legal and gives out = 0, lse = -inf.
+ */
+attn_status_t attn_lse_combine(const float* part_out, const float* part_lse, int B, int H, int C, int Tq,
+                               int D, attn_dtype_t out_dtype, void* out, float* lse, void* stream);
+
+/* Host helper: number of chunks ceil(S / chunk); -1 if chunk <= 0 or S < 0. */
+int attn_splitkv_num_chunks(int S, int chunk);
+
+/* Host helper: static, human-readable text for a status code. */
+const char* attn_status_string(attn_status_t status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ATTN_PREFIX_H */

@@ -1,0 +1,191 @@
+"""ctypes binding of libattnprefix.so (argument marshalling only).
+
+Every computation runs in the HIP kernels behind the C ABI declared in
+``include/attn_prefix.h``; torch supplies device memory and the current
+stream.  There is no fallback: if the library is missing, or a call returns a
+non-OK status, these functions raise.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+from typing import Optional, Tuple
+
+import torch
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libattnprefix.so")
+
+ATTN_OK = 0
+STATUS_NAMES = {
+    0: "ATTN_OK", 1: "ATTN_ERR_NULLPTR", 2: "ATTN_ERR_SHAPE", 3: "ATTN_ERR_DTYPE", 4: "ATTN_ERR_UNSUPPORTED",
+    5: "ATTN_ERR_ALIGN", 6: "ATTN_ERR_CHUNK", 7: "ATTN_ERR_HIP", 8: "ATTN_ERR_ARG",
+}
+ATTN_BF16, ATTN_F32 = 0, 1
+EXPORTED = ("attn_version", "attn_prefix_fwd", "attn_splitkv_partial", "attn_lse_combine",
+            "attn_splitkv_num_chunks", "attn_status_string")
+
+_lib = None
+
+
+class AttnError(RuntimeError):
+    def __init__(self, fn: str, code: int, text: str):
+        super().__init__(f"{fn} failed: {STATUS_NAMES.get(code, code)} ({text})")
+        self.code = code
+
+
+def load() -> ctypes.CDLL:
+    """Load the HIP library once; raise if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is missing: build it with `python -m long_context_prefix_amd.build` "
+                          "(the attention path has no fallback)")
+    L = ctypes.CDLL(LIB_PATH)
+    vp, i32, f32 = ctypes.c_void_p, ctypes.c_int, ctypes.c_float
+    L.attn_version.restype = i32
+    L.attn_version.argtypes = []
+    L.attn_prefix_fwd.restype = i32
+    L.attn_prefix_fwd.argtypes = [vp, vp, vp, vp, i32, i32, i32, i32, i32, f32, i32, vp, vp, vp]
+    L.attn_splitkv_partial.restype = i32
+    L.attn_splitkv_partial.argtypes = [vp, vp, vp, vp, i32, i32, i32, i32, i32, f32, i32, i32, vp, vp, vp]
+    L.attn_lse_combine.restype = i32
+    L.attn_lse_combine.argtypes = [vp, vp, i32, i32, i32, i32, i32, i32, vp, vp, vp]
+    L.attn_splitkv_num_chunks.restype = i32
+    L.attn_splitkv_num_chunks.argtypes = [i32, i32]
+    L.attn_status_string.restype = ctypes.c_char_p
+    L.attn_status_string.argtypes = [i32]
+    _lib = L
+    return L
+
+
+def status_string(code: int) -> str:
+    return load().attn_status_string(int(code)).decode()
+
+
+def _check(fn: str, code: int) -> None:
+    if code != ATTN_OK:
+        raise AttnError(fn, code, status_string(code))
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return ATTN_BF16
+    if t.dtype == torch.float32:
+        return ATTN_F32
+    raise ValueError(f"unsupported dtype {t.dtype} (bf16 or fp32)")
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None or t.numel() == 0 else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(device: torch.device):
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _require(t: torch.Tensor, name: str, device: torch.device) -> None:
+    if t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def attn_splitkv_num_chunks(S: int, chunk: int) -> int:
+    return int(load().attn_splitkv_num_chunks(int(S), int(chunk)))
+
+
+def _fwd_shapes(q, k, v, kv_len):
+    if q.dim() != 4 or k.dim() != 4 or v.dim() != 4:
+        raise ValueError("q, k, v must be [B, H, T, D]")
+    B, H, Tq, D = q.shape
+    if k.shape != v.shape or k.shape[0] != B or k.shape[1] != H or k.shape[3] != D:
+        raise ValueError(f"shape mismatch: q {tuple(q.shape)}, k {tuple(k.shape)}, v {tuple(v.shape)}")
+    if k.dtype != q.dtype or v.dtype != q.dtype:
+        raise ValueError("q, k, v must share one dtype")
+    if kv_len.dtype != torch.int32 or kv_len.shape != (B,):
+        raise ValueError("kv_len must be int32 [B]")
+    dev = q.device
+    if dev.type != "cuda":
+        raise ValueError("tensors must live on a GPU")
+    for t, name in ((q, "q"), (k, "k"), (v, "v"), (kv_len, "kv_len")):
+        _require(t, name, dev)
+    return B, H, Tq, k.shape[2], D, dev
+
+
+def attn_prefix_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, kv_len: torch.Tensor,
+                    scale: Optional[float] = None, out: Optional[torch.Tensor] = None,
+                    lse: Optional[torch.Tensor] = None, return_lse: bool = True) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """Fused prefix-masked attention; returns (out [B,H,Tq,D], lse [B,H,Tq] fp32 or None)."""
+    B, H, Tq, S, D, dev = _fwd_shapes(q, k, v, kv_len)
+    scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None and return_lse:
+        lse = torch.empty((B, H, Tq), dtype=torch.float32, device=dev)
+    _require(out, "out", dev)
+    if out.shape != q.shape or out.dtype != q.dtype:
+        raise ValueError("out must match q in shape and dtype")
+    if lse is not None:
+        _require(lse, "lse", dev)
+        if lse.shape != (B, H, Tq) or lse.dtype != torch.float32:
+            raise ValueError("lse must be fp32 [B, H, Tq]")
+    code = load().attn_prefix_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(kv_len), B, H, Tq, S, D, scale,
+                                  _dtype_code(q), _ptr(out), _ptr(lse), _stream(dev))
+    _check("attn_prefix_fwd", code)
+    return out, lse
+
+
+def attn_splitkv_partial(q, k, v, kv_len, chunk: int, scale: Optional[float] = None,
+                         part_out: Optional[torch.Tensor] = None, part_lse: Optional[torch.Tensor] = None):
+    """Per-chunk fp32 partials; returns (part_out [B,H,C,Tq,D], part_lse [B,H,C,Tq])."""
+    B, H, Tq, S, D, dev = _fwd_shapes(q, k, v, kv_len)
+    scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
+    if chunk <= 0:
+        raise ValueError("chunk must be positive")
+    C = -(-S // chunk)
+    if part_out is None:
+        part_out = torch.empty((B, H, C, Tq, D), dtype=torch.float32, device=dev)
+    if part_lse is None:
+        part_lse = torch.empty((B, H, C, Tq), dtype=torch.float32, device=dev)
+    _require(part_out, "part_out", dev)
+    _require(part_lse, "part_lse", dev)
+    if part_out.shape != (B, H, C, Tq, D) or part_lse.shape != (B, H, C, Tq):
+        raise ValueError("partial buffers have the wrong shape")
+    if part_out.dtype != torch.float32 or part_lse.dtype != torch.float32:
+        raise ValueError("partial buffers must be fp32")
+    code = load().attn_splitkv_partial(_ptr(q), _ptr(k), _ptr(v), _ptr(kv_len), B, H, Tq, S, D, scale,
+                                       _dtype_code(q), int(chunk), _ptr(part_out), _ptr(part_lse), _stream(dev))
+    _check("attn_splitkv_partial", code)
+    return part_out, part_lse
+
+
+def attn_lse_combine(part_out: torch.Tensor, part_lse: torch.Tensor, out_dtype=torch.bfloat16,
+                     out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
+                     return_lse: bool = True):
+    """Exact LSE merge of partials [B,H,C,Tq,D]; returns (out [B,H,Tq,D], lse [B,H,Tq])."""
+    if part_out.dim() != 5 or part_lse.dim() != 4 or part_out.shape[:4] != part_lse.shape:
+        raise ValueError("part_out must be [B,H,C,Tq,D] and part_lse [B,H,C,Tq]")
+    B, H, C, Tq, D = part_out.shape
+    dev = part_out.device
+    _require(part_out, "part_out", dev)
+    _require(part_lse, "part_lse", dev)
+    if out is None:
+        out = torch.empty((B, H, Tq, D), dtype=out_dtype, device=dev)
+    if lse is None and return_lse:
+        lse = torch.empty((B, H, Tq), dtype=torch.float32, device=dev)
+    _require(out, "out", dev)
+    if lse is not None:
+        _require(lse, "lse", dev)
+    code = load().attn_lse_combine(_ptr(part_out), _ptr(part_lse), B, H, C, Tq, D, _dtype_code(out), _ptr(out),
+                                   _ptr(lse), _stream(dev))
+    _check("attn_lse_combine", code)
+    return out, lse
+
+
+def splitkv_fwd(q, k, v, kv_len, chunk: int, scale: Optional[float] = None, return_lse: bool = True):
+    """Split-KV attention: per-chunk partials, then the exact merge (two launches, one stream)."""
+    po, pl = attn_splitkv_partial(q, k, v, kv_len, chunk, scale)
+    return attn_lse_combine(po, pl, q.dtype, return_lse=return_lse)

@@ -1,0 +1,201 @@
+// C ABI of libattnprefix.so: host-side validation, template choice and launch.
+// Every argument check runs before the first HIP call, so a bad call returns
+// its status code without touching the device.
+
+#include <math.h>
+#include <stdio.h>
+#include <stdlib.h>
+
+#include "attn_kernels.hpp"
+#include "attn_prefix.h"
+
+using namespace lcp;
+
+namespace {
+
+constexpr int64_t kMaxI32 = 2147483647;
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
+
+bool verbose() {
+  static int v = -1;
+  if (v < 0) {
+    const char* e = getenv("ATTN_PREFIX_VERBOSE");
+    v = (e && e[0] && e[0] != '0') ? 1 : 0;
+  }
+  return v == 1;
+}
+
+int esize(attn_dtype_t dt) { return dt == ATTN_F32 ? 4 : 2; }
+
+// Checks shared by the fused and the split-KV forward.  On success *noop tells
+// whether the call has no work at all (B, H or Tq is zero).
+attn_status_t check_fwd(const void* q, const void* k, const void* v, const int32_t* kv_len, int B, int H,
+                        int Tq, int S, int D, float scale, attn_dtype_t dtype, const void* out,
+                        const void* out2, bool out2_required, int chunk_or_zero, bool split, bool* noop) {
+  *noop = false;
+  if (dtype != ATTN_BF16 && dtype != ATTN_F32) return ATTN_ERR_DTYPE;
+  if (B < 0 || H < 0 || Tq < 0 || S < 0 || D < 0) return ATTN_ERR_SHAPE;
+  if (split && (chunk_or_zero <= 0 || chunk_or_zero % kBN != 0)) return ATTN_ERR_CHUNK;
+  if (D != 64 && D != 128 && D != 256) return ATTN_ERR_UNSUPPORTED;
+  if (!isfinite(scale)) return ATTN_ERR_ARG;
+  if (B == 0 || H == 0 || Tq == 0) {
+    *noop = true;
+    return ATTN_OK;
+  }
+  if (!q || !kv_len || !out || (out2_required && !out2)) return ATTN_ERR_NULLPTR;
+  if (S > 0 && (!k || !v)) return ATTN_ERR_NULLPTR;
+  if (!aligned16(q) || !aligned16(out) || (out2 && !aligned4(out2)) || !aligned4(kv_len)) return ATTN_ERR_ALIGN;
+  if (S > 0 && (!aligned16(k) || !aligned16(v))) return ATTN_ERR_ALIGN;
+  if ((int64_t)S * D * esize(dtype) > kMaxI32) return ATTN_ERR_SHAPE;
+  const int64_t nqt = ((int64_t)Tq + kBM - 1) / kBM;
+  int64_t grid = nqt * B * H;
+  if (split) grid *= ((int64_t)S + chunk_or_zero - 1) / chunk_or_zero;
+  if (grid > kMaxI32) return ATTN_ERR_SHAPE;
+  return ATTN_OK;
+}
+
+template <class P, int D, bool PARTIAL, int W>
+attn_status_t launch_fwd(const FwdArgs& a, int64_t grid, hipStream_t stream, const char* tag) {
+  if (verbose())
+    fprintf(stderr, "[attn_prefix] %s D=%d %s grid=%lld block=%d lds=%d waves_per_eu=%d\n", tag, D,
+            P::kIsF32 ? "f32" : "bf16", (long long)grid, kThreads, P::LDS_BYTES, W);
+  (void)hipGetLastError();  // clear an error left by unrelated earlier calls
+  hipLaunchKernelGGL((attn_fwd_kernel<P, D, PARTIAL, W>), dim3((unsigned)grid), dim3(kThreads), 0, stream, a);
+  return hipGetLastError() == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
+}
+
+template <bool PARTIAL>
+attn_status_t dispatch_fwd(const FwdArgs& a, int D, attn_dtype_t dtype, int64_t grid, hipStream_t s) {
+  const char* tag = PARTIAL ? "splitkv_partial" : "prefix_fwd";
+  if (dtype == ATTN_BF16) {
+    switch (D) {
+      case 64: return launch_fwd<Bf16Path<64>, 64, PARTIAL, 2>(a, grid, s, tag);
+      case 128: return launch_fwd<Bf16Path<128>, 128, PARTIAL, 2>(a, grid, s, tag);
+      case 256: return launch_fwd<Bf16Path<256>, 256, PARTIAL, 1>(a, grid, s, tag);
+    }
+  } else {
+    switch (D) {
+      case 64: return launch_fwd<F32Path<64>, 64, PARTIAL, 1>(a, grid, s, tag);
+      case 128: return launch_fwd<F32Path<128>, 128, PARTIAL, 1>(a, grid, s, tag);
+      case 256: return launch_fwd<F32Path<256>, 256, PARTIAL, 1>(a, grid, s, tag);
+    }
+  }
+  return ATTN_ERR_UNSUPPORTED;
+}
+
+}  // namespace
+
+extern "C" {
+
+int attn_version(void) { return (0 << 16) | (1 << 8) | 0; }
+
+int attn_splitkv_num_chunks(int S, int chunk) {
+  if (chunk <= 0 || S < 0) return -1;
+  return (int)(((int64_t)S + chunk - 1) / chunk);
+}
+
+const char* attn_status_string(attn_status_t s) {
+  switch (s) {
+    case ATTN_OK: return "ok";
+    case ATTN_ERR_NULLPTR: return "a required pointer is NULL";
+    case ATTN_ERR_SHAPE: return "a size is negative or exceeds the library limits";
+    case ATTN_ERR_DTYPE: return "unknown dtype (expected ATTN_BF16 or ATTN_F32)";
+    case ATTN_ERR_UNSUPPORTED: return "unsupported head dim (supported: 64, 128, 256)";
+    case ATTN_ERR_ALIGN: return "a tensor pointer is misaligned (16 bytes required; 4 for kv_len and lse)";
+    case ATTN_ERR_CHUNK: return "chunk must be a positive multiple of 64";
+    case ATTN_ERR_HIP: return "the HIP runtime reported an error";
+    case ATTN_ERR_ARG: return "a scalar argument is out of range";
+  }
+  return "unknown status";
+}
+
+attn_status_t attn_prefix_fwd(const void* q, const void* k, const void* v, const int32_t* kv_len, int B, int H,
+                              int Tq, int S, int D, float scale, attn_dtype_t dtype, void* out, float* lse,
+                              void* stream) {
+  bool noop = false;
+  attn_status_t st = check_fwd(q, k, v, kv_len, B, H, Tq, S, D, scale, dtype, out, lse, false, 0, false, &noop);
+  if (st != ATTN_OK || noop) return st;
+  FwdArgs a{};
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.kv_len = kv_len;
+  a.B = B;
+  a.H = H;
+  a.Tq = Tq;
+  a.S = S;
+  a.scale_log2 = scale * kLog2e;
+  a.chunk = 0;
+  a.C = 1;
+  a.n_qtiles = (Tq + kBM - 1) / kBM;
+  a.out = out;
+  a.lse = lse;
+  const int64_t grid = (int64_t)a.n_qtiles * B * H;
+  return dispatch_fwd<false>(a, D, dtype, grid, reinterpret_cast<hipStream_t>(stream));
+}
+
+attn_status_t attn_splitkv_partial(const void* q, const void* k, const void* v, const int32_t* kv_len, int B,
+                                   int H, int Tq, int S, int D, float scale, attn_dtype_t dtype, int chunk,
+                                   float* part_out, float* part_lse, void* stream) {
+  bool noop = false;
+  attn_status_t st =
+      check_fwd(q, k, v, kv_len, B, H, Tq, S, D, scale, dtype, part_out, part_lse, true, chunk, true, &noop);
+  if (st != ATTN_OK || noop) return st;
+  const int C = attn_splitkv_num_chunks(S, chunk);
+  if (C == 0) return ATTN_OK;  // S == 0: the partial tensors have no element
+  FwdArgs a{};
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.kv_len = kv_len;
+  a.B = B;
+  a.H = H;
+  a.Tq = Tq;
+  a.S = S;
+  a.scale_log2 = scale * kLog2e;
+  a.chunk = chunk;
+  a.C = C;
+  a.n_qtiles = (Tq + kBM - 1) / kBM;
+  a.part_out = part_out;
+  a.part_lse = part_lse;
+  const int64_t grid = (int64_t)a.n_qtiles * C * B * H;
+  return dispatch_fwd<true>(a, D, dtype, grid, reinterpret_cast<hipStream_t>(stream));
+}
+
+attn_status_t attn_lse_combine(const float* part_out, const float* part_lse, int B, int H, int C, int Tq, int D,
+                               attn_dtype_t out_dtype, void* out, float* lse, void* stream) {
+  if (out_dtype != ATTN_BF16 && out_dtype != ATTN_F32) return ATTN_ERR_DTYPE;
+  if (B < 0 || H < 0 || C < 0 || Tq < 0 || D < 0) return ATTN_ERR_SHAPE;
+  if (D != 64 && D != 128 && D != 256) return ATTN_ERR_UNSUPPORTED;
+  if (B == 0 || H == 0 || Tq == 0) return ATTN_OK;
+  if (!out || (C > 0 && (!part_out || !part_lse))) return ATTN_ERR_NULLPTR;
+  if (!aligned16(out) || (lse && !aligned4(lse))) return ATTN_ERR_ALIGN;
+  if (C > 0 && (!aligned16(part_out) || !aligned4(part_lse))) return ATTN_ERR_ALIGN;
+  const int64_t rows = (int64_t)B * H * Tq;
+  const int rows_per_wg = 1024 / D;
+  const int64_t grid = (rows + rows_per_wg - 1) / rows_per_wg;
+  if (grid > kMaxI32) return ATTN_ERR_SHAPE;
+  CombineArgs a{part_out, part_lse, rows, C, Tq, out, lse};
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  if (verbose())
+    fprintf(stderr, "[attn_prefix] lse_combine D=%d C=%d %s grid=%lld\n", D, C, out_dtype == ATTN_F32 ? "f32" : "bf16",
+            (long long)grid);
+  (void)hipGetLastError();
+#define LCP_COMBINE(DD, F32)                                                                                  \
+  hipLaunchKernelGGL((lse_combine_kernel<DD, F32>), dim3((unsigned)grid), dim3(256), 0, s, a)
+  if (out_dtype == ATTN_F32) {
+    if (D == 64) LCP_COMBINE(64, true);
+    else if (D == 128) LCP_COMBINE(128, true);
+    else LCP_COMBINE(256, true);
+  } else {
+    if (D == 64) LCP_COMBINE(64, false);
+    else if (D == 128) LCP_COMBINE(128, false);
+    else LCP_COMBINE(256, false);
+  }
+#undef LCP_COMBINE
+  return hipGetLastError() == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
+}
+
+}  // extern "C"

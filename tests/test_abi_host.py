@@ -1,0 +1,162 @@
+"""Host-side checks of the C ABI (no GPU needed, no kernel launched).
+
+The library must load, export every function ``include/attn_prefix.h``
+declares, and reject every bad argument with its documented status code before
+any HIP call (the ABI calls below pass fake, never-dereferenced addresses).
+"""
+
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+import torch
+
+from long_context_prefix_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "attn_prefix.h")
+
+OK, NULLPTR, SHAPE, DTYPE, UNSUP, ALIGN, CHUNK, HIP, ARG = range(9)
+BF16, F32 = 0, 1
+P = ctypes.c_void_p(4096)  # aligned fake device address; never dereferenced on these paths
+PM = ctypes.c_void_p(4096 + 8)  # misaligned for 16-byte tensors
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(attn_[a-z0-9_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def L():
+    return _lib.load()
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    assert names == sorted(_lib.EXPORTED), names
+
+
+def test_every_declared_symbol_is_exported(L):
+    for name in declared_functions():
+        assert hasattr(L, name), name
+    nm = subprocess.run(["nm", "-D", "--defined-only", _lib.LIB_PATH], capture_output=True, text=True)
+    if nm.returncode == 0:
+        exported = set(line.split()[-1] for line in nm.stdout.splitlines() if " T " in line)
+        for name in declared_functions():
+            assert name in exported, name
+
+
+def test_version_and_chunks(L):
+    assert L.attn_version() == (0 << 16) | (1 << 8)
+    assert L.attn_splitkv_num_chunks(102400, 4096) == 25
+    assert L.attn_splitkv_num_chunks(4096, 4096) == 1
+    assert L.attn_splitkv_num_chunks(4097, 4096) == 2
+    assert L.attn_splitkv_num_chunks(0, 64) == 0
+    assert L.attn_splitkv_num_chunks(10, 0) == -1
+    assert L.attn_splitkv_num_chunks(-1, 64) == -1
+
+
+def test_status_strings(L):
+    for code in range(9):
+        s = _lib.status_string(code)
+        assert s and s != "unknown status"
+    assert _lib.status_string(99) == "unknown status"
+
+
+def fwd(L, q=P, k=P, v=P, kv=P, B=1, H=1, Tq=1, S=1, D=64, scale=0.125, dt=BF16, out=P, lse=None):
+    return L.attn_prefix_fwd(q, k, v, kv, B, H, Tq, S, D, scale, dt, out, lse, None)
+
+
+def split(L, q=P, k=P, v=P, kv=P, B=1, H=1, Tq=1, S=64, D=64, scale=0.125, dt=BF16, chunk=64, po=P, pl=P):
+    return L.attn_splitkv_partial(q, k, v, kv, B, H, Tq, S, D, scale, dt, chunk, po, pl, None)
+
+
+def combine(L, po=P, pl=P, B=1, H=1, C=2, Tq=1, D=64, dt=BF16, out=P, lse=None):
+    return L.attn_lse_combine(po, pl, B, H, C, Tq, D, dt, out, lse, None)
+
+
+def test_prefix_fwd_argument_errors(L):
+    assert fwd(L, dt=2) == DTYPE
+    assert fwd(L, dt=-1) == DTYPE
+    for bad in (dict(B=-1), dict(H=-1), dict(Tq=-1), dict(S=-1), dict(D=-64)):
+        assert fwd(L, **bad) == SHAPE, bad
+    for d in (0, 32, 96, 100, 512):
+        assert fwd(L, D=d) == UNSUP, d
+    assert fwd(L, scale=float("nan")) == ARG
+    assert fwd(L, scale=float("inf")) == ARG
+    # precedence: dtype before shape before head dim before scale
+    assert fwd(L, dt=5, B=-1, D=7) == DTYPE
+    assert fwd(L, B=-1, D=7) == SHAPE
+    assert fwd(L, D=7, scale=float("nan")) == UNSUP
+    for name in ("q", "kv", "out"):
+        assert fwd(L, **{name: None}) == NULLPTR, name
+    assert fwd(L, k=None) == NULLPTR
+    assert fwd(L, v=None) == NULLPTR
+    for name in ("q", "k", "v", "out"):
+        assert fwd(L, **{name: PM}) == ALIGN, name
+    assert fwd(L, kv=ctypes.c_void_p(4098)) == ALIGN
+    assert fwd(L, lse=ctypes.c_void_p(4097)) == ALIGN
+    # limits: per-(b,h) K/V slice beyond 2^31 bytes, or too many workgroups
+    assert fwd(L, S=2**22, D=256) == SHAPE
+    assert fwd(L, S=2**22, D=256, dt=F32) == SHAPE
+    assert fwd(L, B=2**16, H=2**16, Tq=128) == SHAPE
+
+
+def test_prefix_fwd_empty_calls_are_noops(L):
+    # zero-sized batches, heads or queries: no work, pointers may be NULL
+    for z in (dict(B=0), dict(H=0), dict(Tq=0)):
+        assert fwd(L, q=None, k=None, v=None, kv=None, out=None, **z) == OK, z
+    # S = 0 with nothing to read: k and v may be NULL (not launched here: B = 0)
+    assert fwd(L, B=0, S=0, k=None, v=None) == OK
+
+
+def test_splitkv_argument_errors(L):
+    assert split(L, chunk=0) == CHUNK
+    assert split(L, chunk=-64) == CHUNK
+    assert split(L, chunk=96) == CHUNK
+    assert split(L, chunk=100) == CHUNK
+    assert split(L, dt=3) == DTYPE
+    assert split(L, D=48) == UNSUP
+    assert split(L, po=None) == NULLPTR
+    assert split(L, pl=None) == NULLPTR
+    assert split(L, po=PM) == ALIGN
+    assert split(L, pl=ctypes.c_void_p(4098)) == ALIGN
+    assert split(L, B=0, po=None, pl=None) == OK
+    assert split(L, S=2**20, chunk=64, B=2**14, H=8) == SHAPE  # 2^31 workgroups
+
+
+def test_combine_argument_errors(L):
+    assert combine(L, dt=7) == DTYPE
+    assert combine(L, C=-1) == SHAPE
+    assert combine(L, D=32) == UNSUP
+    assert combine(L, out=None) == NULLPTR
+    assert combine(L, po=None) == NULLPTR
+    assert combine(L, pl=None) == NULLPTR
+    assert combine(L, out=PM) == ALIGN
+    assert combine(L, po=PM) == ALIGN
+    assert combine(L, lse=ctypes.c_void_p(4097)) == ALIGN
+    assert combine(L, B=0, out=None) == OK
+
+
+def test_binding_rejects_bad_tensors_before_the_abi():
+    q = torch.zeros(1, 1, 4, 64, dtype=torch.bfloat16)
+    kv = torch.tensor([4], dtype=torch.int32)
+    with pytest.raises(ValueError):
+        _lib.attn_prefix_fwd(q, q, q, kv)  # CPU tensors
+    with pytest.raises(ValueError):
+        _lib.attn_prefix_fwd(q, q[..., :32], q, kv)
+    with pytest.raises(ValueError):
+        _lib.attn_prefix_fwd(q, q, q, kv.to(torch.int64))
+    with pytest.raises(ValueError):
+        _lib.attn_prefix_fwd(q.half(), q.half(), q.half(), kv)
+
+
+def test_missing_library_fails_loudly(monkeypatch, tmp_path):
+    monkeypatch.setattr(_lib, "_lib", None)
+    monkeypatch.setattr(_lib, "LIB_PATH", str(tmp_path / "absent.so"))
+    with pytest.raises(ImportError):
+        _lib.load()

@@ -1,0 +1,243 @@
+"""GPU parity of the HIP kernels against the fp64 oracle, through the C ABI.
+
+Small cases span several 128-row query tiles and 64-key tiles with ragged
+tails; the edge matrix covers n in {0, 1, 63, 64, 65, S}, T_q in {1, 17, 128,
+129} and D in {64, 128, 256}.  Bitwise properties (padding invariance,
+determinism, n = 1) and guard-byte checks follow.  Full-size workloads are in
+``test_gpu_workloads.py``.
+"""
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+from long_context_prefix_amd import _lib
+from long_context_prefix_amd.workloads import WORKLOADS, make_inputs, make_workload
+from oracle import ref_lse_combine, ref_prefix_fwd, ref_splitkv_partial
+from tests.parity import assert_parity, log, to64
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda"
+
+
+def _np(t):
+    return to64(t)
+
+
+def _run_fused(q, k, v, kv, scale):
+    out, lse = _lib.attn_prefix_fwd(q, k, v, kv, scale)
+    torch.cuda.synchronize()
+    return out, lse
+
+
+def _oracle(q, k, v, kv, scale):
+    return ref_prefix_fwd(_np(q), _np(k), _np(v), kv.cpu().numpy(), scale)
+
+
+@pytest.mark.parametrize("D", [64, 128, 256])
+@pytest.mark.parametrize("Tq", [1, 17, 128, 129])
+def test_edge_matrix_bf16(D, Tq):
+    S = 200
+    lens = [0, 1, 63, 64, 65, S]
+    log(f"edge bf16 D={D} Tq={Tq} S={S} lens={lens}")
+    q, k, v, kv = make_inputs(len(lens), 2, Tq, S, D, lens, "bf16", 1.0, seed=100 + D + Tq, device=DEV)
+    scale = 1.0 / math.sqrt(D)
+    out, lse = _run_fused(q, k, v, kv, scale)
+    ro, rl = _oracle(q, k, v, kv, scale)
+    assert_parity(out, lse, ro, rl, "bf16", f"edge D={D} Tq={Tq}")
+
+
+@pytest.mark.parametrize("D", [64, 128, 256])
+def test_multi_tile_bf16_sharp(D):
+    """Several query and key tiles, ragged tails, peaky attention (q scaled x4)."""
+    B, H, Tq, S = 2, 3, 300, 777
+    lens = [700, 777]
+    log(f"sharp bf16 D={D}")
+    q, k, v, kv = make_inputs(B, H, Tq, S, D, lens, "bf16", 1.0, seed=200 + D, device=DEV)
+    q.mul_(4.0)
+    scale = 1.0 / math.sqrt(D)
+    out, lse = _run_fused(q, k, v, kv, scale)
+    ro, rl = _oracle(q, k, v, kv, scale)
+    assert_parity(out, lse, ro, rl, "bf16", f"sharp D={D}")
+
+
+@pytest.mark.parametrize("D", [64, 128, 256])
+def test_fp32_inputs(D):
+    B, H, Tq, S = 2, 2, 150, 300
+    lens = [0 if D == 64 else 1, 257]
+    log(f"fp32 D={D}")
+    q, k, v, kv = make_inputs(B, H, Tq, S, D, lens, "f32", 1.0, seed=300 + D, device=DEV)
+    scale = 1.0 / math.sqrt(D)
+    out, lse = _run_fused(q, k, v, kv, scale)
+    ro, rl = _oracle(q, k, v, kv, scale)
+    assert_parity(out, lse, ro, rl, "f32", f"fp32 D={D}")
+
+
+def test_tiny_prefix_mask_workload():
+    w = WORKLOADS["tiny_prefix_mask"]
+    log("tiny_prefix_mask workload")
+    q, k, v, kv = make_workload(w, device=DEV)
+    out, lse = _run_fused(q, k, v, kv, w.scale)
+    ro, rl = _oracle(q, k, v, kv, w.scale)
+    assert_parity(out, lse, ro, rl, "f32", "tiny_prefix_mask")
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("chunk", [64, 128, 192])
+def test_splitkv_partial_and_combine(dtype, chunk):
+    D = 128
+    B, H, Tq, S = 3, 2, 130, 450
+    lens = [0, 129, 450]
+    log(f"splitkv dtype={dtype} chunk={chunk}")
+    q, k, v, kv = make_inputs(B, H, Tq, S, D, lens, dtype, 1.0, seed=400 + chunk, device=DEV)
+    scale = 1.0 / math.sqrt(D)
+    po, pl = _lib.attn_splitkv_partial(q, k, v, kv, chunk, scale)
+    torch.cuda.synchronize()
+    rpo, rpl = ref_splitkv_partial(_np(q), _np(k), _np(v), np.array(lens), scale, chunk)
+    assert po.shape == rpo.shape
+    assert_parity(po, pl, rpo, rpl, dtype, f"partials {dtype} chunk={chunk}")
+    # the merge kernel alone, on the GPU's own partials, fp32 output
+    mo, ml = _lib.attn_lse_combine(po, pl, torch.float32)
+    torch.cuda.synchronize()
+    eo, el = ref_lse_combine(_np(po), _np(pl), axis=2)
+    o, lg = _np(mo), _np(ml)
+    assert np.array_equal(np.isneginf(lg), np.isneginf(el))
+    fin = ~np.isneginf(el)
+    assert np.abs(o - eo).max() <= 1e-5
+    assert np.abs(lg[fin] - el[fin]).max() <= 1e-5
+    # end to end against the single-pass oracle
+    out, lse = _lib.splitkv_fwd(q, k, v, kv, chunk, scale)
+    torch.cuda.synchronize()
+    ro, rl = _oracle(q, k, v, kv, scale)
+    assert_parity(out, lse, ro, rl, dtype, f"split end-to-end {dtype} chunk={chunk}")
+    if dtype == "f32":
+        # fp32 inputs: exact products on both paths, so split and fused agree to fp32 round-off
+        fo, fl = _run_fused(q, k, v, kv, scale)
+        assert np.abs(_np(fo) - _np(out)).max() <= 2e-6
+        a, b = _np(fl), _np(lse)
+        assert np.array_equal(np.isneginf(a), np.isneginf(b))
+        m = np.isfinite(a)
+        assert np.abs(a[m] - b[m]).max() <= 2e-6
+
+
+def test_combine_edge_cases():
+    D = 64
+    # every partial -inf -> (0, -inf); C = 0 -> (0, -inf)
+    po = torch.randn(1, 2, 3, 5, D, device=DEV)
+    pl = torch.full((1, 2, 3, 5), -math.inf, device=DEV)
+    pl[0, 1, 1, 2] = 0.5
+    out, lse = _lib.attn_lse_combine(po, pl, torch.float32)
+    torch.cuda.synchronize()
+    o, l = _np(out), _np(lse)
+    assert np.all(o[0, 0] == 0) and np.all(np.isneginf(l[0, 0]))
+    np.testing.assert_allclose(o[0, 1, 2], _np(po)[0, 1, 1, 2], rtol=0, atol=1e-6)
+    assert abs(l[0, 1, 2] - 0.5) < 1e-6
+    empty_o = torch.empty(1, 2, 0, 5, D, device=DEV)
+    empty_l = torch.empty(1, 2, 0, 5, device=DEV)
+    out, lse = _lib.attn_lse_combine(empty_o, empty_l, torch.bfloat16)
+    torch.cuda.synchronize()
+    assert torch.all(out == 0) and torch.all(torch.isneginf(lse))
+
+
+@pytest.mark.parametrize("D", [128, 256])
+def test_padding_invariance_bitwise(D):
+    """Pads never read: no pads, +-1e4 pads and NaN pads give identical bits."""
+    B, H, Tq, n = 2, 2, 70, 333
+    log(f"padding invariance D={D}")
+    q, k, v, kv = make_inputs(B, H, Tq, n, D, [n, 129], "bf16", 1.0, seed=500 + D, device=DEV)
+    base_o, base_l = _run_fused(q, k, v, kv, 0.1)
+    for pad, S in ((1e4, n + 77), (float("nan"), n + 200)):
+        kp = torch.empty(B, H, S, D, dtype=k.dtype, device=DEV).fill_(pad)
+        vp = torch.empty_like(kp).fill_(pad)
+        kp[:, :, :n] = k
+        vp[:, :, :n] = v
+        # element 1 has n = 129, so k[:, :, 129:n] are pads already in the base call
+        o, l = _run_fused(q, kp, vp, kv, 0.1)
+        assert torch.equal(o, base_o), f"pad={pad}"
+        assert torch.equal(l, base_l), f"pad={pad}"
+        po1, pl1 = _lib.attn_splitkv_partial(q, k, v, kv, 128, 0.1)
+        po2, pl2 = _lib.attn_splitkv_partial(q, kp, vp, kv, 128, 0.1)
+        torch.cuda.synchronize()
+        C1 = po1.shape[2]
+        assert torch.equal(po1, po2[:, :, :C1]) and torch.equal(pl1, pl2[:, :, :C1])
+        assert torch.all(po2[:, :, C1:] == 0) and torch.all(torch.isneginf(pl2[:, :, C1:]))
+
+
+def test_determinism_bitwise():
+    q, k, v, kv = make_inputs(2, 4, 300, 1000, 256, [1000, 517], "bf16", 0.7, seed=600, device=DEV)
+    o1, l1 = _run_fused(q, k, v, kv, 0.0625)
+    o2, l2 = _run_fused(q, k, v, kv, 0.0625)
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_n_equals_one_is_exact(dtype):
+    D = 128
+    q, k, v, kv = make_inputs(2, 2, 40, 90, D, [1, 1], dtype, 1.0, seed=700, device=DEV)
+    out, lse = _run_fused(q, k, v, kv, 0.2)
+    assert torch.equal(out, v[:, :, :1].expand_as(out))
+    expect = 0.2 * torch.einsum("bhtd,bhd->bht", q.double().cpu(), k[:, :, 0].double().cpu())
+    assert (lse.double().cpu() - expect).abs().max().item() <= 1e-4
+
+
+def test_n_zero_and_empty_slots():
+    q, k, v, kv = make_inputs(2, 2, 40, 64, 64, [0, 0], "bf16", 1.0, seed=800, device=DEV, pad=float("nan"))
+    out, lse = _run_fused(q, k, v, kv, 0.125)
+    assert torch.all(out == 0) and torch.all(torch.isneginf(lse))
+    k0 = torch.empty(2, 2, 0, 64, dtype=torch.bfloat16, device=DEV)
+    out, lse = _run_fused(q, k0, k0, kv, 0.125)
+    assert torch.all(out == 0) and torch.all(torch.isneginf(lse))
+
+
+def test_kv_len_out_of_range_is_clamped():
+    q, k, v, kv = make_inputs(2, 1, 20, 100, 64, [100, 5], "bf16", 1.0, seed=900, device=DEV)
+    bad = torch.tensor([1000, -7], dtype=torch.int32, device=DEV)
+    out, lse = _run_fused(q, k, v, bad, 0.125)
+    ro, rl = _oracle(q, k, v, torch.tensor([100, 0], dtype=torch.int32), 0.125)
+    assert_parity(out, lse, ro, rl, "bf16", "clamped kv_len")
+
+
+def test_guard_bytes_untouched():
+    B, H, Tq, S, D = 2, 2, 130, 300, 128
+    q, k, v, kv = make_inputs(B, H, Tq, S, D, [300, 65], "bf16", 1.0, seed=1000, device=DEV)
+    G = 4096
+    n_out, n_lse = B * H * Tq * D, B * H * Tq
+    out_buf = torch.full((n_out + G,), 7.0, dtype=torch.bfloat16, device=DEV)
+    lse_buf = torch.full((n_lse + G,), 7.0, dtype=torch.float32, device=DEV)
+    _lib.attn_prefix_fwd(q, k, v, kv, 0.1, out=out_buf[:n_out].view(B, H, Tq, D), lse=lse_buf[:n_lse].view(B, H, Tq))
+    C = -(-S // 64)
+    n_po, n_pl = B * H * C * Tq * D, B * H * C * Tq
+    po_buf = torch.full((n_po + G,), 7.0, dtype=torch.float32, device=DEV)
+    pl_buf = torch.full((n_pl + G,), 7.0, dtype=torch.float32, device=DEV)
+    _lib.attn_splitkv_partial(q, k, v, kv, 64, 0.1, part_out=po_buf[:n_po].view(B, H, C, Tq, D),
+                              part_lse=pl_buf[:n_pl].view(B, H, C, Tq))
+    torch.cuda.synchronize()
+    for buf, n in ((out_buf, n_out), (lse_buf, n_lse), (po_buf, n_po), (pl_buf, n_pl)):
+        assert torch.all(buf[n:] == 7.0)
+        assert not torch.any(torch.isnan(buf[:n]))
+
+
+def test_no_device_allocation():
+    """The library allocates nothing: free device memory is unchanged by a call."""
+    q, k, v, kv = make_inputs(1, 8, 1024, 4096, 256, [4000], "bf16", 1.0, seed=1100, device=DEV)
+    out = torch.empty_like(q)
+    lse = torch.empty(1, 8, 1024, dtype=torch.float32, device=DEV)
+    po = torch.empty(1, 8, 2, 1024, 256, dtype=torch.float32, device=DEV)
+    pl = torch.empty(1, 8, 2, 1024, dtype=torch.float32, device=DEV)
+    for _ in range(2):  # the first launches load the code objects; measure after them
+        _lib.attn_prefix_fwd(q, k, v, kv, 0.1, out=out, lse=lse)
+        _lib.attn_splitkv_partial(q, k, v, kv, 2048, 0.1, part_out=po, part_lse=pl)
+        _lib.attn_lse_combine(po, pl, torch.bfloat16, out=out, lse=lse)
+    torch.cuda.synchronize()
+    free0, _ = torch.cuda.mem_get_info()
+    alloc0 = torch.cuda.memory_allocated()
+    _lib.attn_prefix_fwd(q, k, v, kv, 0.1, out=out, lse=lse)
+    _lib.attn_splitkv_partial(q, k, v, kv, 2048, 0.1, part_out=po, part_lse=pl)
+    _lib.attn_lse_combine(po, pl, torch.bfloat16, out=out, lse=lse)
+    torch.cuda.synchronize()
+    free1, _ = torch.cuda.mem_get_info()
+    assert torch.cuda.memory_allocated() == alloc0
+    assert free1 == free0
