@@ -1,0 +1,271 @@
+#!/usr/bin/env python3
+"""Benchmark of the prefix-masked attention path on one MI355X.
+
+A timed step is one fused prefix-masked forward (work bounds, Q tile, K/V
+stream, QK^T, online softmax, PV, epilogue) over the 121k-key ICL block:
+B=1, H=8, D=256, T_q=131,072 queries, n=121,000 valid keys of S=131,072 slots,
+bf16 inputs, fp32 softmax.  ``value`` counts only valid keys:
+FLOP = 4 * D * H * T_q * sum_b n_b.
+
+The split-KV rows (per-chunk partials plus the LSE merge) run in the same
+process at their own workload -- 160 sequences x 4 heads, D=128, 128 queries,
+100,000 valid keys of 102,400, 4,096-key chunks -- and are reported in the
+``splitkv`` object in GB/s of algorithmic bytes (Q + valid K + valid V + out +
+lse; the fp32 partial round trip is implementation overhead, not counted).
+
+Inputs are seeded synthetic tensors already resident in HBM when timing
+starts.  Kernel durations come from HIP events on the stream the kernels are
+launched on.  The CPU baseline times the fp64 oracle on a bounded sample of
+query rows of the same workload, and the same rows check parity of the timed
+output.
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import re
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0      # MI355X HBM3E
+
+
+def log(msg: str) -> None:
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for rel in ("long_context_prefix_amd/csrc/attn_kernels.hpp", "long_context_prefix_amd/csrc/attn_api.hip"):
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_from_profile(name: str, src_hash: str):
+    """HBM bytes per launch from a committed rocprofv3 counter summary, if it is current."""
+    path = os.path.join(ROOT, "profiles", name)
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    m_hash = re.search(r"kernel_source_sha256_16:\s*([0-9a-f]+)", text)
+    m_bytes = re.search(r"hbm_bytes_per_launch:\s*([0-9.eE+]+)", text)
+    if not m_hash or not m_bytes or m_hash.group(1) != src_hash:
+        return None
+    return float(m_bytes.group(1))
+
+
+def time_launches(fn, steps: int, torch):
+    """Run fn() `steps` times with HIP events around each call on the current stream."""
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s, e in evs:
+        s.record()
+        fn()
+        e.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    return wall, [s.elapsed_time(e) for s, e in evs]
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--no-splitkv", action="store_true", help="skip the split-KV workload")
+    ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle timing and parity sample")
+    ap.add_argument("--cpu-rows", type=int, default=64, help="oracle query rows per head for the CPU baseline")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run one 1 GiB device copy (reference kernel for HBM counter scaling)")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(run with --gpus 1)", file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+
+    from long_context_prefix_amd import _lib
+    from long_context_prefix_amd.workloads import WORKLOADS, make_workload, sample_rows
+
+    _lib.load()  # fails loudly when the HIP library is missing
+    torch.cuda.set_device(0)
+    src_hash = kernel_source_hash()
+
+    # ------------------------------------------------------------- fused path
+    w = WORKLOADS["icl_121k"]
+    log(f"generating {w.name}: B={w.B} H={w.H} D={w.D} Tq={w.Tq} S={w.S} kv_len={w.lens().tolist()}")
+    q, k, v, kv = make_workload(w, device="cuda")
+    out = torch.empty_like(q)
+    lse = torch.empty((w.B, w.H, w.Tq), dtype=torch.float32, device="cuda")
+    lens = w.lens()
+    flops = 4.0 * w.D * w.H * w.Tq * float(lens.sum())
+
+    def fused():
+        _lib.attn_prefix_fwd(q, k, v, kv, w.scale, out=out, lse=lse)
+
+    for _ in range(args.warmup):
+        fused()
+    torch.cuda.synchronize()
+    log(f"timing {args.steps} fused steps")
+    wall, ms = time_launches(fused, args.steps, torch)
+    ms_avg = sum(ms) / len(ms)
+    value = flops * args.steps / wall / 1e12
+    achieved = flops / (ms_avg * 1e-3) / 1e12
+    log(f"fused: {ms_avg:.3f} ms/launch (min {min(ms):.3f}), {achieved:.1f} TFLOP/s, wall {wall:.3f} s")
+
+    traffic = traffic_from_profile("attn_fwd_icl_121k_traffic.md", src_hash)
+    roofline = {
+        "bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+        "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": traffic,
+        "kernel": "attn_fwd_kernel<Bf16Path<256>>", "avg_launch_ms": round(ms_avg, 4),
+        "algorithmic_flop_per_launch": flops,
+    }
+
+    result = {
+        "metric": "prefix-masked attention TFLOP/s (valid keys, bf16, d=256) and % MFMA peak",
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall / args.steps * 1e3, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded normals, +-1e4 in padded key slots)",
+        "config": {"workload": w.name, "B": w.B, "H": w.H, "head_dim": w.D, "T_q": w.Tq, "S": w.S,
+                   "kv_len": [int(x) for x in lens], "scale": w.scale, "pct_mfma_peak": round(100 * value / PEAK_BF16_TFLOPS, 2)},
+        "roofline": roofline,
+        "kernel_source_sha256_16": src_hash,
+    }
+
+    # -------------------------------------------------- CPU baseline + parity
+    if not args.no_cpu_baseline:
+        from oracle import ref_prefix_fwd  # test infrastructure: used only for this leg
+
+        try:
+            from threadpoolctl import threadpool_info
+
+            blas_threads = max([p.get("num_threads", 0) for p in threadpool_info()] + [0])
+        except Exception:  # pragma: no cover
+            blas_threads = 0
+        cores = len(os.sched_getaffinity(0))
+        rows = sample_rows(w.seed, w.Tq, args.cpu_rows, w.B * w.H)
+        log(f"oracle on {rows.shape[1]} rows x {w.B * w.H} heads (cores={cores}, blas_threads={blas_threads})")
+        idx = torch.as_tensor(rows, device="cuda").view(w.B, w.H, -1)
+        q_s = torch.gather(q, 2, idx[..., None].expand(-1, -1, -1, w.D)).float().cpu().numpy()
+        k_h = k[:, :, : int(lens.max())].float().cpu().numpy()
+        v_h = v[:, :, : int(lens.max())].float().cpu().numpy()
+        t0 = time.perf_counter()
+        ro, rl = ref_prefix_fwd(q_s, k_h, v_h, lens, w.scale)
+        t_cpu = time.perf_counter() - t0
+        sample_flops = 4.0 * w.D * rows.size * float(lens.max())
+        result["cpu_baseline"] = {
+            "value": round(sample_flops / t_cpu / 1e12, 6), "unit": "TFLOP/s", "cores": int(blas_threads or cores),
+            "kind": "oracle",
+            "sample": f"fp64 numpy oracle on {rows.shape[1]} seeded query rows per head x {w.B * w.H} heads "
+                      f"against all {int(lens.max())} valid keys ({sample_flops:.3e} FLOP in {t_cpu:.2f} s)",
+        }
+        go = torch.gather(out, 2, idx[..., None].expand(-1, -1, -1, w.D)).double().cpu().numpy()
+        gl = torch.gather(lse, 2, idx).double().cpu().numpy()
+        d = go - ro
+        result["parity"] = {
+            "rows_checked": int(rows.size),
+            "out_max_abs": float(np.abs(d).max()),
+            "out_rel_l2": float(np.linalg.norm(d) / np.linalg.norm(ro)),
+            "lse_max_abs": float(np.abs(gl - rl).max()),
+            "tolerance": "max_abs <= 2e-2 and rel_l2 <= 5e-3 (bf16), lse <= 1e-3",
+        }
+        log(f"parity: {result['parity']}")
+        del k_h, v_h
+
+    del q, k, v, out, lse
+    torch.cuda.empty_cache()
+
+    # ------------------------------------------------------------- split-KV
+    if not args.no_splitkv:
+        ws = WORKLOADS["inducing_splitkv"]
+        log(f"generating {ws.name}: B={ws.B} H={ws.H} D={ws.D} Tq={ws.Tq} S={ws.S} n=100000 chunk={ws.chunk}")
+        q, k, v, kv = make_workload(ws, device="cuda")
+        C = -(-ws.S // ws.chunk)
+        po = torch.empty((ws.B, ws.H, C, ws.Tq, ws.D), dtype=torch.float32, device="cuda")
+        pl = torch.empty((ws.B, ws.H, C, ws.Tq), dtype=torch.float32, device="cuda")
+        out = torch.empty_like(q)
+        lse = torch.empty((ws.B, ws.H, ws.Tq), dtype=torch.float32, device="cuda")
+        slens = ws.lens()
+        esz = 2
+        alg_bytes = float(ws.B * ws.H * (2 * ws.Tq * ws.D * esz + ws.Tq * 4)) + float(2 * ws.H * ws.D * esz * slens.sum())
+        part_bytes = float(po.numel() * 4 + pl.numel() * 4)
+
+        def partial():
+            _lib.attn_splitkv_partial(q, k, v, kv, ws.chunk, ws.scale, part_out=po, part_lse=pl)
+
+        def combine():
+            _lib.attn_lse_combine(po, pl, torch.bfloat16, out=out, lse=lse)
+
+        for _ in range(args.warmup):
+            partial()
+            combine()
+        torch.cuda.synchronize()
+        steps = max(1, args.steps)
+        log(f"timing {steps} split-KV steps")
+        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+        t0 = time.perf_counter()
+        for e0, e1, e2 in evs:
+            e0.record()
+            partial()
+            e1.record()
+            combine()
+            e2.record()
+        torch.cuda.synchronize()
+        wall_s = time.perf_counter() - t0
+        t_part = sum(a.elapsed_time(b) for a, b, _ in evs) / steps
+        t_comb = sum(b.elapsed_time(c) for _, b, c in evs) / steps
+        gbs = alg_bytes / ((t_part + t_comb) * 1e-3) / 1e9
+        part_gbs = (alg_bytes - float(ws.B * ws.H * (ws.Tq * ws.D * esz + ws.Tq * 4)) + part_bytes) / (t_part * 1e-3) / 1e9
+        log(f"split-KV: partial {t_part:.3f} ms, combine {t_comb:.3f} ms, {gbs:.0f} GB/s algorithmic")
+        result["splitkv"] = {
+            "workload": ws.name, "B": ws.B, "H": ws.H, "head_dim": ws.D, "T_q": ws.Tq, "S": ws.S, "n": int(slens[0]),
+            "chunk": ws.chunk, "chunks": C,
+            "value": round(gbs, 1), "unit": "GB/s (algorithmic: Q + valid K/V + out + lse)",
+            "pct_hbm_peak": round(100 * gbs / PEAK_HBM_GBS, 2),
+            "ms_per_step": round(wall_s / steps * 1e3, 4), "partial_ms": round(t_part, 4), "combine_ms": round(t_comb, 4),
+            "alg_bytes": alg_bytes, "partial_roundtrip_bytes": 2 * part_bytes,
+            "tflops_valid_keys": round(4.0 * ws.D * ws.H * ws.Tq * float(slens.sum()) / ((t_part + t_comb) * 1e-3) / 1e12, 2),
+            "roofline_partial_kernel": {
+                "bound": "hbm", "achieved": round(part_gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": round(part_gbs / PEAK_HBM_GBS, 4),
+                "traffic": traffic_from_profile("attn_splitkv_partial_inducing_traffic.md", src_hash),
+                "bytes_counted": "Q + valid K/V + fp32 partial write",
+            },
+        }
+        del q, k, v, po, pl, out, lse
+        torch.cuda.empty_cache()
+
+    if args.copy_calibration:
+        src = torch.empty(1 << 28, dtype=torch.float32, device="cuda").fill_(1.0)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        log("copy calibration: 1 GiB read + 1 GiB written")
+
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,61 @@
+"""Full-size workloads on the GPU, in the launch configurations the benchmark times.
+
+The oracle cannot afford every output at these sizes, so it checks seeded
+samples of query rows (always including the first and the last row) and, for
+the split-KV workload, whole sequences (the first, the last and seeded ones).
+"""
+
+import numpy as np
+import pytest
+import torch
+
+from long_context_prefix_amd import _lib
+from long_context_prefix_amd.workloads import WORKLOADS, make_workload, sample_rows
+from oracle import ref_prefix_fwd, ref_splitkv_partial
+from tests.parity import assert_parity, gather_rows, log, to64
+
+pytestmark = [pytest.mark.gpu, pytest.mark.slow]
+
+DEV = "cuda"
+
+
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("name,rows", [("icl_16k", 256), ("ragged_32k", 128), ("icl_121k", 128)])
+def test_fused_workload_sampled_rows(name, rows):
+    w = WORKLOADS[name]
+    lens = w.lens()
+    log(f"workload {name}: B={w.B} H={w.H} D={w.D} Tq={w.Tq} S={w.S} kv_len={lens.tolist()}")
+    q, k, v, kv = make_workload(w, device=DEV)
+    out, lse = _lib.attn_prefix_fwd(q, k, v, kv, w.scale)
+    torch.cuda.synchronize()
+    sel = sample_rows(w.seed, w.Tq, rows, w.B * w.H)
+    q_s = to64(gather_rows(q, sel))
+    nmax = int(lens.max())
+    ro, rl = ref_prefix_fwd(q_s, to64(k[:, :, :nmax]), to64(v[:, :, :nmax]), lens, w.scale)
+    assert_parity(gather_rows(out, sel), gather_rows(lse, sel), ro, rl, "bf16", name)
+
+
+@pytest.mark.timeout(900)
+def test_inducing_splitkv_workload():
+    w = WORKLOADS["inducing_splitkv"]
+    lens = w.lens()
+    log(f"workload {w.name}: B={w.B} H={w.H} D={w.D} Tq={w.Tq} S={w.S} n={lens[0]} chunk={w.chunk}")
+    q, k, v, kv = make_workload(w, device=DEV)
+    po, pl = _lib.attn_splitkv_partial(q, k, v, kv, w.chunk, w.scale)
+    out, lse = _lib.attn_lse_combine(po, pl, torch.bfloat16)
+    fo, fl = _lib.attn_prefix_fwd(q, k, v, kv, w.scale)
+    torch.cuda.synchronize()
+    assert po.shape[2] == 25
+    rng = np.random.default_rng(w.seed)
+    seqs = sorted(set([0, w.B - 1] + rng.choice(np.arange(1, w.B - 1), size=6, replace=False).tolist()))
+    for b in seqs:
+        n = int(lens[b])
+        qb, kb, vb = to64(q[b:b + 1]), to64(k[b:b + 1, :, :n]), to64(v[b:b + 1, :, :n])
+        ro, rl = ref_prefix_fwd(qb, kb, vb, [n], w.scale)
+        assert_parity(out[b:b + 1], lse[b:b + 1], ro, rl, "bf16", f"split-KV seq {b}")
+        assert_parity(fo[b:b + 1], fl[b:b + 1], ro, rl, "bf16", f"fused seq {b}")
+        if b == w.B - 1:
+            # the last valid chunk holds 1,696 keys; compare it on its own
+            rpo, rpl = ref_splitkv_partial(qb, to64(k[b:b + 1]), to64(v[b:b + 1]), [n], w.scale, w.chunk)
+            assert_parity(po[b:b + 1, :, 24], pl[b:b + 1, :, 24], rpo[:, :, 24], rpl[:, :, 24], "bf16",
+                          f"partial chunk 24 seq {b}")
