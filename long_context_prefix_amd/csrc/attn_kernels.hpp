@@ -81,6 +81,22 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, p);
 }
 
+// Raw buffer resource over [base, base + bytes) (gfx9-family descriptor word 3).
+// The arguments are workgroup-uniform; readfirstlane keeps the descriptor in SGPRs (a
+// descriptor in VGPRs would need a waterfall loop around every load).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  const uint64_t p = reinterpret_cast<uint64_t>(base);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)p);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(p >> 32));
+  const uint32_t n = __builtin_amdgcn_readfirstlane(bytes);
+  void* b = reinterpret_cast<void*>(((uint64_t)hi << 32) | lo);
+  return __builtin_amdgcn_make_buffer_rsrc(b, (short)0, (int)n, 0x00020000);
+}
+
+__device__ __forceinline__ u32x4 buf_load16(__amdgpu_buffer_rsrc_t rs, uint32_t off) {
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, (int)off, 0, 0));
+}
+
 // ---------------------------------------------------------------- bf16 path
 // K tile in LDS row-major [kBN][D + 8]; V^T tile [D][kBN + 8] with permuted
 // key positions.  The 16-byte row padding puts the 8 lanes of one LDS access
@@ -97,7 +113,6 @@ struct Bf16Path {
   static constexpr bool kIsF32 = false;
 
   struct QFrag { bf16x8 v[NQ]; };
-  struct Stage { u32x4 k[NCH]; u32x4 v[KPT]; };
 
   __device__ static void load_q(QFrag& f, const uint16_t* qrow, bool valid, int h) {
 #pragma unroll
@@ -108,33 +123,39 @@ struct Bf16Path {
     }
   }
 
-  // Global -> registers for keys [t0, t0 + nv) of this (b, h); rows >= nv become zero.
-  __device__ static void load_tile(Stage& st, const uint16_t* kb, const uint16_t* vb, int64_t t0, int nv, int tid) {
+  // Global -> registers for one tile through a buffer resource that covers exactly the tile's
+  // valid rows: a row at or past the valid count lies outside the resource, so its load
+  // returns zero without touching memory and the code stays branch-free.
+  __device__ static void load_k(u32x4 (&st)[NCH], __amdgpu_buffer_rsrc_t rs, int tid) {
 #pragma unroll
     for (int i = 0; i < NCH; ++i) {
-      int c = tid + kThreads * i;
-      int key = c / (D / 8), dg = c % (D / 8);
-      u32x4 x = {0u, 0u, 0u, 0u};
-      if (key < nv) x = *reinterpret_cast<const u32x4*>(kb + (t0 + key) * D + dg * 8);
-      st.k[i] = x;
-    }
-    int kgrp = tid % KGRP, dg = tid / KGRP;
-#pragma unroll
-    for (int e = 0; e < KPT; ++e) {
-      int key = vt_pos(kgrp * KPT + e);
-      u32x4 x = {0u, 0u, 0u, 0u};
-      if (key < nv) x = *reinterpret_cast<const u32x4*>(vb + (t0 + key) * D + dg * 8);
-      st.v[e] = x;
+      const int c = tid + kThreads * i;
+      const int key = c / (D / 8), dg = c % (D / 8);
+      st[i] = buf_load16(rs, (uint32_t)(key * D * 2 + dg * 16));
     }
   }
 
-  __device__ static void store_tile(const Stage& st, uint16_t* ks, uint16_t* vt, int tid) {
+  // Each thread loads KPT keys x 8 columns of V, the keys that land next to each other in
+  // the permuted V^T layout, so that the transpose in store_v stays inside the thread.
+  __device__ static void load_v(u32x4 (&st)[KPT], __amdgpu_buffer_rsrc_t rs, int tid) {
+    const int kgrp = tid % KGRP, dg = tid / KGRP;
+#pragma unroll
+    for (int e = 0; e < KPT; ++e) {
+      const int key = vt_pos(kgrp * KPT + e);
+      st[e] = buf_load16(rs, (uint32_t)(key * D * 2 + dg * 16));
+    }
+  }
+
+  __device__ static void store_k(const u32x4 (&st)[NCH], uint16_t* ks, int tid) {
 #pragma unroll
     for (int i = 0; i < NCH; ++i) {
       int c = tid + kThreads * i;
       int key = c / (D / 8), dg = c % (D / 8);
-      *reinterpret_cast<u32x4*>(ks + key * KSTR + dg * 8) = st.k[i];
+      *reinterpret_cast<u32x4*>(ks + key * KSTR + dg * 8) = st[i];
     }
+  }
+
+  __device__ static void store_v(const u32x4 (&st)[KPT], uint16_t* vt, int tid) {
     int kgrp = tid % KGRP, dg = tid / KGRP;
     // 8 x KPT transpose: row i of the output holds element i of each loaded chunk.
 #pragma unroll
@@ -142,7 +163,7 @@ struct Bf16Path {
       uint32_t w[KPT / 2];
 #pragma unroll
       for (int t = 0; t < KPT / 2; ++t) {
-        uint32_t a = st.v[2 * t][i >> 1], b = st.v[2 * t + 1][i >> 1];
+        uint32_t a = st[2 * t][i >> 1], b = st[2 * t + 1][i >> 1];
         w[t] = (i & 1) ? ((a >> 16) | (b & 0xffff0000u)) : ((a & 0xffffu) | (b << 16));
       }
       uint16_t* dst = vt + (dg * 8 + i) * VSTR + kgrp * KPT;
@@ -171,16 +192,13 @@ struct Bf16Path {
     }
   }
 
-  // O^T += V^T P^T with P rounded to bf16 as the MFMA operand.
-  __device__ static void accumulate(f32x16 (&o)[D / 32], const f32x16 (&p)[kBN / 32], const uint16_t* vt, int lane) {
+  // O^T += V^T P^T.  pk[ks] holds P for keys 16*ks .. 16*ks+15 of the tile as the B operand
+  // (bf16, in S^T register order).
+  __device__ static void accumulate(f32x16 (&o)[D / 32], const u32x4 (&pk)[kBN / 16], const uint16_t* vt, int lane) {
     const int i = lane & 31, h = lane >> 5;
 #pragma unroll
     for (int ks = 0; ks < kBN / 16; ++ks) {
-      const f32x16& pk = p[ks >> 1];
-      const int r0 = 8 * (ks & 1);
-      u32x4 pw = {pack_bf16x2(pk[r0 + 0], pk[r0 + 1]), pack_bf16x2(pk[r0 + 2], pk[r0 + 3]),
-                  pack_bf16x2(pk[r0 + 4], pk[r0 + 5]), pack_bf16x2(pk[r0 + 6], pk[r0 + 7])};
-      bf16x8 pb = __builtin_bit_cast(bf16x8, pw);
+      const bf16x8 pb = __builtin_bit_cast(bf16x8, pk[ks]);
 #pragma unroll
       for (int db = 0; db < D / 32; ++db) {
         bf16x8 a = *reinterpret_cast<const bf16x8*>(vt + (32 * db + i) * VSTR + 16 * ks + 8 * h);
@@ -278,69 +296,99 @@ struct F32Path {
   }
 };
 
-// ------------------------------------------------------------ the fwd kernel
+// ------------------------------------------------------------ the fwd kernels
 // Workgroup id -> (query tile, [chunk], head, batch), query tile fastest, so
 // the workgroups resident at one time walk the same (b, h) key stream and
 // share it through L2.
-template <class P, int D, bool PARTIAL>
-__device__ __forceinline__ void attn_fwd_body(const FwdArgs& a, char* smem) {
-  using Elem = typename std::conditional<P::kIsF32, float, uint16_t>::type;
-  const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
-  const int h_half = lane >> 5;
+struct Work {
+  int b, h, c, lo, hi, row;
+  bool row_ok;
+  int64_t bh, out_row;
+};
 
+template <bool PARTIAL>
+__device__ __forceinline__ Work decode(const FwdArgs& a, int lane, int wave) {
+  Work w;
   int wg = blockIdx.x;
   const int qt = wg % a.n_qtiles;
   wg /= a.n_qtiles;
-  int c = 0;
+  w.c = 0;
   if (PARTIAL) {
-    c = wg % a.C;
+    w.c = wg % a.C;
     wg /= a.C;
   }
-  const int h = wg % a.H;
-  const int b = wg / a.H;
-
-  int n = a.kv_len[b];
-  n = n < 0 ? 0 : (n > a.S ? a.S : n);
-  int lo = 0, hi = n;
+  w.h = wg % a.H;
+  w.b = wg / a.H;
+  int n = a.kv_len[w.b];
+  n = n < 0 ? 0 : (n > a.S ? a.S : n);  // out-of-range lengths are clamped, never trusted
+  w.lo = 0;
+  w.hi = n;
   if (PARTIAL) {
-    lo = c * a.chunk;
-    hi = min(lo + a.chunk, n);
+    w.lo = w.c * a.chunk;
+    w.hi = min(w.lo + a.chunk, n);
   }
+  w.bh = (int64_t)w.b * a.H + w.h;
+  w.row = qt * kBM + wave * 32 + (lane & 31);
+  w.row_ok = w.row < a.Tq;
+  w.out_row = PARTIAL ? ((w.bh * a.C + w.c) * a.Tq + w.row) : (w.bh * a.Tq + w.row);
+  return w;
+}
 
-  const int64_t bh = (int64_t)b * a.H + h;
-  const int row = qt * kBM + wave * 32 + (lane & 31);
-  const bool row_ok = row < a.Tq;
-  const int64_t out_row = PARTIAL ? ((bh * a.C + c) * a.Tq + row) : (bh * a.Tq + row);
-
-  if (hi <= lo) {  // no valid key: out = 0, lse = -inf
-    if (row_ok) {
+// Epilogue: out = O / l (or the fp32 partial) and lse = ln sum exp.  A row
+// without any valid key (o = 0, inv_l = 0, lse = -inf) writes zeros.
+template <class P, int D, bool PARTIAL>
+__device__ __forceinline__ void write_rows(const FwdArgs& a, const Work& w, const f32x16 (&o)[D / 32], float inv_l,
+                                           float lse_nat, int h_half) {
+  if (!w.row_ok) return;
 #pragma unroll
-      for (int db = 0; db < D / 32; ++db)
+  for (int db = 0; db < D / 32; ++db)
 #pragma unroll
-        for (int rg = 0; rg < 4; ++rg) {
-          const int64_t off = out_row * D + 32 * db + 8 * rg + 4 * h_half;
-          if (PARTIAL)
-            *reinterpret_cast<f32x4*>(a.part_out + off) = f32x4{0.f, 0.f, 0.f, 0.f};
-          else
-            P::store_out4(a.out, off, 0.f, 0.f, 0.f, 0.f);
-        }
-      if (h_half == 0) {
-        if (PARTIAL) a.part_lse[out_row] = -__builtin_inff();
-        else if (a.lse) a.lse[out_row] = -__builtin_inff();
-      }
+    for (int rg = 0; rg < 4; ++rg) {
+      const int64_t off = w.out_row * D + 32 * db + 8 * rg + 4 * h_half;
+      const float x0 = o[db][4 * rg + 0] * inv_l, x1 = o[db][4 * rg + 1] * inv_l;
+      const float x2 = o[db][4 * rg + 2] * inv_l, x3 = o[db][4 * rg + 3] * inv_l;
+      if (PARTIAL)
+        *reinterpret_cast<f32x4*>(a.part_out + off) = f32x4{x0, x1, x2, x3};
+      else
+        P::store_out4(a.out, off, x0, x1, x2, x3);
     }
+  if (h_half == 0) {
+    if (PARTIAL) a.part_lse[w.out_row] = lse_nat;
+    else if (a.lse) a.lse[w.out_row] = lse_nat;
+  }
+}
+
+template <class P, int D, bool PARTIAL>
+__device__ __forceinline__ void write_empty(const FwdArgs& a, const Work& w, int h_half) {
+  f32x16 z[D / 32];
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db) z[db] = f32x16{};
+  write_rows<P, D, PARTIAL>(a, w, z, 0.0f, -__builtin_inff(), h_half);
+}
+
+// Plain tile loop (fp32 inputs): one LDS buffer, register prefetch of the next
+// tile, softmax rescaled every tile.
+template <class P, int D, bool PARTIAL>
+__device__ __forceinline__ void attn_fwd_body(const FwdArgs& a, char* smem) {
+  using Elem = float;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int h_half = lane >> 5;
+  const Work w = decode<PARTIAL>(a, lane, wave);
+  if (w.hi <= w.lo) {
+    write_empty<P, D, PARTIAL>(a, w, h_half);
     return;
   }
+  const int lo = w.lo, hi = w.hi;
 
-  const Elem* qrow = reinterpret_cast<const Elem*>(a.q) + (bh * a.Tq + (row_ok ? row : 0)) * D;
-  const Elem* kbase = reinterpret_cast<const Elem*>(a.k) + bh * a.S * D;
-  const Elem* vbase = reinterpret_cast<const Elem*>(a.v) + bh * a.S * D;
+  const Elem* qrow = reinterpret_cast<const Elem*>(a.q) + (w.bh * a.Tq + (w.row_ok ? w.row : 0)) * D;
+  const Elem* kbase = reinterpret_cast<const Elem*>(a.k) + w.bh * a.S * D;
+  const Elem* vbase = reinterpret_cast<const Elem*>(a.v) + w.bh * a.S * D;
   Elem* ks = reinterpret_cast<Elem*>(smem);
   Elem* vs = ks + kBN * P::KSTR;
 
   typename P::QFrag qf;
-  P::load_q(qf, qrow, row_ok, h_half);
+  P::load_q(qf, qrow, w.row_ok, h_half);
 
   f32x16 o[D / 32];
 #pragma unroll
@@ -392,33 +440,182 @@ __device__ __forceinline__ void attn_fwd_body(const FwdArgs& a, char* smem) {
 
     P::accumulate(o, s, vs, lane);
   }
+  write_rows<P, D, PARTIAL>(a, w, o, 1.0f / l, (m + __builtin_amdgcn_logf(l)) * kLn2, h_half);
+}
 
-  if (!row_ok) return;
-  const float inv_l = 1.0f / l;
-  const float lse_nat = (m + __builtin_amdgcn_logf(l)) * kLn2;
+// Online-softmax state of one lane (one query row, half of its keys).  The
+// running max m is kept in the scaled log2 domain and is moved only when a
+// tile's max exceeds it by more than kRescaleLog2: probabilities are computed
+// against a possibly stale max, so p <= 2^kRescaleLog2, and the final O / l is
+// unchanged because O and l share that max.  Rescaling O (kept in AGPRs) is
+// therefore rare instead of once per tile.
+constexpr float kRescaleLog2 = 8.0f;
+
+template <int D>
+struct Softmax {
+  float m = -__builtin_inff();  // scaled log2-domain max the probabilities are taken against
+  float l = 0.0f;               // this lane's partial row sum (lanes l and l^32 are added at the end)
+
+  // Row max of raw scores s (rows keys of this lane), rescale if it moved too far.
+  __device__ __forceinline__ void update_max(const f32x16 (&s)[kBN / 32], float c, f32x16 (&o)[D / 32]) {
+    float mt = fmaxf(s[0][0], s[0][1]);
 #pragma unroll
-  for (int db = 0; db < D / 32; ++db)
+    for (int kb = 0; kb < kBN / 32; ++kb)
 #pragma unroll
-    for (int rg = 0; rg < 4; ++rg) {
-      const int64_t off = out_row * D + 32 * db + 8 * rg + 4 * h_half;
-      const float x0 = o[db][4 * rg + 0] * inv_l, x1 = o[db][4 * rg + 1] * inv_l;
-      const float x2 = o[db][4 * rg + 2] * inv_l, x3 = o[db][4 * rg + 3] * inv_l;
-      if (PARTIAL)
-        *reinterpret_cast<f32x4*>(a.part_out + off) = f32x4{x0, x1, x2, x3};
-      else
-        P::store_out4(a.out, off, x0, x1, x2, x3);
+      for (int r = (kb == 0 ? 2 : 0); r < 16; ++r) mt = fmaxf(mt, s[kb][r]);
+    mt = pair_max(mt) * c;
+    const bool need = mt > m + kRescaleLog2;
+    if (__builtin_amdgcn_ballot_w64(need) != 0) {  // wave-uniform and rare
+      const float m_new = fmaxf(m, mt);
+      const float alpha = __builtin_amdgcn_exp2f(m - m_new);
+      m = m_new;
+      l *= alpha;
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) o[db][r] *= alpha;
     }
-  if (h_half == 0) {
-    if (PARTIAL) a.part_lse[out_row] = lse_nat;
-    else if (a.lse) a.lse[out_row] = lse_nat;
   }
+
+  // p = 2^(c*s - m), rounded to bf16 pairs in S^T register order; masked keys give p = 0.
+  template <bool MASK>
+  __device__ __forceinline__ void exp_pack(const f32x16 (&s)[kBN / 32], float c, u32x4 (&pk)[kBN / 16], int nv,
+                                           int h_half) {
+    const float nm = -m;
+    float acc[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < kBN / 16; ++ks) {
+      float p[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int r = 8 * (ks & 1) + e;
+        float x = __builtin_amdgcn_exp2f(__builtin_fmaf(s[ks >> 1][r], c, nm));
+        if (MASK && st_key(ks >> 1, r, h_half) >= nv) x = 0.0f;
+        p[e] = x;
+        acc[e & 3] += x;
+      }
+      pk[ks] = u32x4{pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]), pack_bf16x2(p[4], p[5]),
+                     pack_bf16x2(p[6], p[7])};
+    }
+    l += (acc[0] + acc[1]) + (acc[2] + acc[3]);
+  }
+};
+
+// bf16 path, software pipelined.  At the top of iteration j the scores S_j are
+// in registers, K_{j+1} and V_j are in LDS and K_{j+2}, V_{j+1} are in staging
+// registers.  Iteration j issues S_{j+1} = K_{j+1} Q^T on the MFMA pipe while
+// the exponentials of tile j run on the VALU, stages K_{j+2} and V_{j+1} into
+// the LDS buffers freed by the previous iteration, starts the global loads of
+// K_{j+3} and V_{j+2}, and accumulates O += V_j P_j.  One barrier per tile.
+template <int D, bool PARTIAL>
+__device__ __forceinline__ void bf16_fwd_pipelined(const FwdArgs& a, char* smem) {
+  using P = Bf16Path<D>;
+  constexpr int K_ELEMS = kBN * P::KSTR, V_ELEMS = D * P::VSTR;
+  uint16_t* const kbuf0 = reinterpret_cast<uint16_t*>(smem);
+  uint16_t* const kbuf1 = kbuf0 + K_ELEMS;
+  uint16_t* const vbuf0 = kbuf1 + K_ELEMS;
+  uint16_t* const vbuf1 = vbuf0 + V_ELEMS;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int h_half = lane >> 5;
+  const Work w = decode<PARTIAL>(a, lane, wave);
+  if (w.hi <= w.lo) {
+    write_empty<P, D, PARTIAL>(a, w, h_half);
+    return;
+  }
+  const int nkeys = w.hi - w.lo;
+  const int T = (nkeys + kBN - 1) / kBN;
+  auto nv_of = [&](int t) {
+    const int r = nkeys - t * kBN;
+    return r < 0 ? 0 : (r > kBN ? kBN : r);
+  };
+
+  const uint16_t* qrow = reinterpret_cast<const uint16_t*>(a.q) + (w.bh * a.Tq + (w.row_ok ? w.row : 0)) * D;
+  const uint16_t* kb = reinterpret_cast<const uint16_t*>(a.k) + (w.bh * a.S + w.lo) * D;
+  const uint16_t* vb = reinterpret_cast<const uint16_t*>(a.v) + (w.bh * a.S + w.lo) * D;
+  // resource over the valid rows of tile t only (nothing past n_b is ever addressable)
+  auto k_tile = [&](int t) { return make_rsrc(kb + (int64_t)t * kBN * D, (uint32_t)nv_of(t) * (D * 2)); };
+  auto v_tile = [&](int t) { return make_rsrc(vb + (int64_t)t * kBN * D, (uint32_t)nv_of(t) * (D * 2)); };
+
+  typename P::QFrag qf;
+  P::load_q(qf, qrow, w.row_ok, h_half);
+  float c = a.scale_log2;
+  if (c < 0.0f) {  // c * (q.k) == |c| * ((-q).k): keep c >= 0 so raw-score maxima are the scaled maxima
+    c = -c;
+#pragma unroll
+    for (int kk = 0; kk < P::NQ; ++kk) {
+      u32x4 x = __builtin_bit_cast(u32x4, qf.v[kk]) ^ 0x80008000u;
+      qf.v[kk] = __builtin_bit_cast(bf16x8, x);
+    }
+  }
+
+  u32x4 sk[P::NCH], sv[P::KPT];
+  P::load_k(sk, k_tile(0), tid);
+  P::load_v(sv, v_tile(0), tid);
+  P::store_k(sk, kbuf0, tid);
+  P::store_v(sv, vbuf0, tid);
+  P::load_k(sk, k_tile(1), tid);
+  P::load_v(sv, v_tile(1), tid);
+  __syncthreads();
+  f32x16 s_cur[kBN / 32];
+  P::scores(s_cur, qf, kbuf0, lane);
+  P::store_k(sk, kbuf1, tid);
+  P::load_k(sk, k_tile(2), tid);
+  __syncthreads();
+
+  f32x16 o[D / 32];
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db) o[db] = f32x16{};
+  Softmax<D> sm;
+  u32x4 pk[kBN / 16];
+
+  for (int j = 0; j < T - 1; ++j) {
+    uint16_t* const k_next = (j & 1) ? kbuf0 : kbuf1;  // K_{j+1}
+    uint16_t* const k_free = (j & 1) ? kbuf1 : kbuf0;  // K_j consumed -> K_{j+2}
+    uint16_t* const v_cur = (j & 1) ? vbuf1 : vbuf0;   // V_j
+    uint16_t* const v_free = (j & 1) ? vbuf0 : vbuf1;  // V_{j-1} consumed -> V_{j+1}
+    sm.update_max(s_cur, c, o);
+    f32x16 s_next[kBN / 32];
+    P::scores(s_next, qf, k_next, lane);
+    sm.template exp_pack<false>(s_cur, c, pk, kBN, h_half);
+    P::store_v(sv, v_free, tid);
+    P::store_k(sk, k_free, tid);
+    P::load_v(sv, v_tile(j + 2), tid);
+    P::load_k(sk, k_tile(j + 3), tid);
+    P::accumulate(o, pk, v_cur, lane);
+    __syncthreads();
+#pragma unroll
+    for (int kb2 = 0; kb2 < kBN / 32; ++kb2) s_cur[kb2] = s_next[kb2];
+  }
+
+  // last tile: S_{T-1} in s_cur, V_{T-1} in vbuf[(T-1) & 1]; mask keys >= nv
+  const int nv_last = nv_of(T - 1);
+  if (nv_last < kBN) {
+#pragma unroll
+    for (int kb2 = 0; kb2 < kBN / 32; ++kb2)
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+        if (st_key(kb2, r, h_half) >= nv_last) s_cur[kb2][r] = -__builtin_inff();
+  }
+  sm.update_max(s_cur, c, o);
+  sm.template exp_pack<true>(s_cur, c, pk, nv_last, h_half);
+  P::accumulate(o, pk, ((T - 1) & 1) ? vbuf1 : vbuf0, lane);
+
+  const float l = pair_sum(sm.l);
+  write_rows<P, D, PARTIAL>(a, w, o, 1.0f / l, (sm.m + __builtin_amdgcn_logf(l)) * kLn2, h_half);
 }
 
 template <class P, int D, bool PARTIAL, int WAVES_PER_EU>
 __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads), amdgpu_waves_per_eu(WAVES_PER_EU, WAVES_PER_EU)))
 void attn_fwd_kernel(FwdArgs a) {
-  __shared__ __attribute__((aligned(16))) char smem[P::LDS_BYTES];
-  attn_fwd_body<P, D, PARTIAL>(a, smem);
+  if constexpr (P::kIsF32) {
+    __shared__ __attribute__((aligned(16))) char smem[P::LDS_BYTES];
+    attn_fwd_body<P, D, PARTIAL>(a, smem);
+  } else {
+    __shared__ __attribute__((aligned(16))) char smem[2 * P::LDS_BYTES];
+    bf16_fwd_pipelined<D, PARTIAL>(a, smem);
+  }
 }
 
 // ------------------------------------------------------------ LSE combine
