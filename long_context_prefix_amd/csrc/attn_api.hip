@@ -71,9 +71,9 @@ attn_status_t dispatch_fwd(const FwdArgs& a, int D, attn_dtype_t dtype, int64_t 
   const char* tag = PARTIAL ? "splitkv_partial" : "prefix_fwd";
   if (dtype == ATTN_BF16) {
     switch (D) {
-      case 64: return launch_fwd<Bf16Path<64>, 64, PARTIAL, 2>(a, grid, s, tag);
-      case 128: return launch_fwd<Bf16Path<128>, 128, PARTIAL, 2>(a, grid, s, tag);
-      case 256: return launch_fwd<Bf16Path<256>, 256, PARTIAL, 1>(a, grid, s, tag);
+      case 64: return launch_fwd<Bf16Dma<64>, 64, PARTIAL, 2>(a, grid, s, tag);
+      case 128: return launch_fwd<Bf16Dma<128>, 128, PARTIAL, 2>(a, grid, s, tag);
+      case 256: return launch_fwd<Bf16Dma<256>, 256, PARTIAL, 1>(a, grid, s, tag);
     }
   } else {
     switch (D) {

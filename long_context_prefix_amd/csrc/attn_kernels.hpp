@@ -17,9 +17,12 @@
 // With the 32x32 MFMA output layout, lane l holds query row (l % 32) and half
 // of the keys of each 32-key block; lanes l and l ^ 32 share a row, so a row
 // max or sum is 16 register ops plus one v_permlane32_swap.  The k index of
-// the P.V contraction is free to follow the S^T register order; V^T is stored
-// in LDS with its key positions permuted to match (bits 2 and 3 of the key
-// index swapped), so every MFMA operand is one 16-byte LDS read.
+// the P.V contraction follows the S^T register order.
+//
+// bf16 inputs: K and V tiles are copied global -> LDS by buffer loads that
+// write LDS directly (no staging registers), K operands are 16-byte LDS reads
+// and V^T operands come from the transposing LDS read; fp32 inputs use a
+// plain register-staged tile loop with fp32 MFMA.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -34,6 +37,7 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(3))) char lds_char;
 
 constexpr int kThreads = 256;  // 4 wavefronts of 64
 constexpr int kBM = 128;       // query rows per workgroup (32 per wave)
@@ -97,22 +101,66 @@ __device__ __forceinline__ u32x4 buf_load16(__amdgpu_buffer_rsrc_t rs, uint32_t 
   return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, (int)off, 0, 0));
 }
 
-// ---------------------------------------------------------------- bf16 path
-// K tile in LDS row-major [kBN][D + 8]; V^T tile [D][kBN + 8] with permuted
-// key positions.  The 16-byte row padding puts the 8 lanes of one LDS access
-// phase on distinct banks for the K and V^T operand reads.
+// ------------------------------------------------------- bf16 path, DMA layout
+// K and V tiles go global -> LDS with 16-byte buffer loads that write LDS
+// directly (lane l of one load fills bytes [16 l, 16 l + 16) of a 1 KB block),
+// so no staging registers and no LDS stores are needed.  A tile of kBN keys
+// is NBLK blocks of 1 KB, each padded to 1040 bytes; a block holds RPB whole
+// key rows.  Which key sits in which block follows from the key's bits
+// j = 32 kb + 16 s + 8 g + 4 h + e (see blk_of / row_of) and is chosen so that
+//   * the QK^T operand read (ds_read_b128: 16 lanes = 16 consecutive keys of
+//     one 32-key block, same column) touches 16 distinct bank groups, and
+//   * the transposing V read (ds_read_b64_tr_b16: a group of 16 lanes reads
+//     4 keys x 32 bytes, lanes l and l+16 the other 32 bytes of the same keys)
+//     covers 256 distinct bytes per 32 lanes,
+// and so that every operand address is one per-lane base plus an immediate.
+// V is read transposed by the hardware: within a 16-lane group, output lane i,
+// element e comes from source lane 4e + i/4, element i%4; source lane 4e + jj
+// reads 4 consecutive columns (4 jj ..) of key e, so output lane i receives
+// column i of 4 keys -- the A operand of V^T P^T with the keys in k order.
 template <int D>
-struct Bf16Path {
-  static constexpr int KSTR = D + 8;    // bf16 elements per K row in LDS
-  static constexpr int VSTR = kBN + 8;  // bf16 elements per V^T row in LDS
-  static constexpr int LDS_BYTES = (kBN * KSTR + D * VSTR) * 2;
-  static constexpr int NCH = D / 32;    // 16-byte chunks per thread per tile, for K and for V
-  static constexpr int KPT = D / 32;    // keys per thread in the V transpose
-  static constexpr int KGRP = kBN / KPT;
-  static constexpr int NQ = D / 16;     // Q^T operand registers (8 bf16 each)
+struct Bf16Dma {
+  static constexpr int ROWB = D * 2;       // bytes per key row
+  static constexpr int RPB = 1024 / ROWB;  // rows per block (2, 4, 8)
+  static constexpr int NBLK = kBN / RPB;   // blocks per tile (32, 16, 8)
+  static constexpr int BLK = 1040;         // padded block stride
+  static constexpr int TILE_BYTES = NBLK * BLK;
+  static constexpr int LDS_BYTES = 4 * TILE_BYTES;  // K and V, two buffers each
+  static constexpr int NQ = D / 16;
+  static constexpr int LPR = ROWB / 16;    // DMA lanes per row
   static constexpr bool kIsF32 = false;
+  static_assert(kBN == 64, "the block layout is written for 64-key tiles");
 
   struct QFrag { bf16x8 v[NQ]; };
+
+  __host__ __device__ static constexpr int blk_of(int j) {
+    const int e = j & 3, h = (j >> 2) & 1, g = (j >> 3) & 1, kb = j >> 5;
+    if constexpr (D == 256) return 16 * kb + 4 * e + 2 * g + h;
+    else if constexpr (D == 128) return 4 * e + 2 * g + h;
+    else return 4 * (e & 1) + 2 * g + h;
+  }
+  __host__ __device__ static constexpr int row_of(int j) {
+    const int e = j & 3, s = (j >> 4) & 1, kb = j >> 5;
+    if constexpr (D == 256) return s;
+    else if constexpr (D == 128) return 2 * kb + s;
+    else return 4 * kb + 2 * s + (e >> 1);
+  }
+  // LDS byte address (within a tile buffer) of key j, byte column col
+  __host__ __device__ static constexpr int addr(int j, int col) { return blk_of(j) * BLK + row_of(j) * ROWB + col; }
+  // the key stored in row r of block b (inverse of blk_of / row_of)
+  __host__ __device__ static constexpr int key_of(int b, int r) {
+    int kb, s, g, h, e;
+    h = b & 1;
+    g = (b >> 1) & 1;
+    if constexpr (D == 256) {
+      kb = b >> 4; e = (b >> 2) & 3; s = r;
+    } else if constexpr (D == 128) {
+      kb = r >> 1; s = r & 1; e = b >> 2;
+    } else {
+      kb = r >> 2; s = (r >> 1) & 1; e = 2 * (r & 1) + (b >> 2);
+    }
+    return 32 * kb + 16 * s + 8 * g + 4 * h + e;
+  }
 
   __device__ static void load_q(QFrag& f, const uint16_t* qrow, bool valid, int h) {
 #pragma unroll
@@ -123,91 +171,65 @@ struct Bf16Path {
     }
   }
 
-  // Global -> registers for one tile through a buffer resource that covers exactly the tile's
-  // valid rows: a row at or past the valid count lies outside the resource, so its load
-  // returns zero without touching memory and the code stays branch-free.
-  __device__ static void load_k(u32x4 (&st)[NCH], __amdgpu_buffer_rsrc_t rs, int tid) {
+  // Issue this wave's share of one tile's DMA (blocks wave, wave+4, ...).  The resource
+  // covers only the tile's valid rows; other lanes write zeros without a fetch.
+  __device__ static void dma_tile(__amdgpu_buffer_rsrc_t rs, lds_char* buf, int wave_u, int lane) {
+    const int r = lane / LPR, ch = lane % LPR;
 #pragma unroll
-    for (int i = 0; i < NCH; ++i) {
-      const int c = tid + kThreads * i;
-      const int key = c / (D / 8), dg = c % (D / 8);
-      st[i] = buf_load16(rs, (uint32_t)(key * D * 2 + dg * 16));
+    for (int bi = 0; bi < NBLK / 4; ++bi) {
+      const int b = wave_u + 4 * bi;
+      const int j = key_of(b, r);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void*)(buf + b * BLK), 16,
+                                               j * ROWB + ch * 16, 0, 0, 0);
     }
   }
 
-  // Each thread loads KPT keys x 8 columns of V, the keys that land next to each other in
-  // the permuted V^T layout, so that the transpose in store_v stays inside the thread.
-  __device__ static void load_v(u32x4 (&st)[KPT], __amdgpu_buffer_rsrc_t rs, int tid) {
-    const int kgrp = tid % KGRP, dg = tid / KGRP;
-#pragma unroll
-    for (int e = 0; e < KPT; ++e) {
-      const int key = vt_pos(kgrp * KPT + e);
-      st[e] = buf_load16(rs, (uint32_t)(key * D * 2 + dg * 16));
-    }
+  // per-lane base of the QK^T operand read (key i = lane % 32 of block kb = 0, chunk h)
+  __device__ static int k_base(int lane) { return addr(lane & 31, 16 * (lane >> 5)); }
+  // per-lane base of the transposing V read (source role: key e of group h, columns 4 jj ..)
+  __device__ static int v_base(int lane) {
+    const int grp = lane >> 4, s16 = lane & 15;
+    const int hv = grp >> 1, dh = grp & 1, e = s16 >> 2, jj = s16 & 3;
+    return addr(4 * hv + e, 32 * dh + 8 * jj);
   }
 
-  __device__ static void store_k(const u32x4 (&st)[NCH], uint16_t* ks, int tid) {
-#pragma unroll
-    for (int i = 0; i < NCH; ++i) {
-      int c = tid + kThreads * i;
-      int key = c / (D / 8), dg = c % (D / 8);
-      *reinterpret_cast<u32x4*>(ks + key * KSTR + dg * 8) = st[i];
-    }
-  }
-
-  __device__ static void store_v(const u32x4 (&st)[KPT], uint16_t* vt, int tid) {
-    int kgrp = tid % KGRP, dg = tid / KGRP;
-    // 8 x KPT transpose: row i of the output holds element i of each loaded chunk.
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      uint32_t w[KPT / 2];
-#pragma unroll
-      for (int t = 0; t < KPT / 2; ++t) {
-        uint32_t a = st[2 * t][i >> 1], b = st[2 * t + 1][i >> 1];
-        w[t] = (i & 1) ? ((a >> 16) | (b & 0xffff0000u)) : ((a & 0xffffu) | (b << 16));
-      }
-      uint16_t* dst = vt + (dg * 8 + i) * VSTR + kgrp * KPT;
-      if constexpr (KPT == 8) {
-        *reinterpret_cast<u32x4*>(dst) = u32x4{w[0], w[1], w[2], w[3]};
-      } else if constexpr (KPT == 4) {
-        *reinterpret_cast<u32x2*>(dst) = u32x2{w[0], w[1]};
-      } else {
-        *reinterpret_cast<uint32_t*>(dst) = w[0];
-      }
-    }
-  }
-
-  // S^T (two 32-key blocks) = K_tile Q^T, fp32 accumulation.
-  __device__ static void scores(f32x16 (&s)[kBN / 32], const QFrag& f, const uint16_t* ks, int lane) {
-    const int i = lane & 31, h = lane >> 5;
+  // S^T (two 32-key blocks) = K_tile Q^T
+  __device__ static void scores(f32x16 (&s)[kBN / 32], const QFrag& f, const lds_char* kt, int kbase) {
 #pragma unroll
     for (int kb = 0; kb < kBN / 32; ++kb) s[kb] = f32x16{};
 #pragma unroll
     for (int kk = 0; kk < NQ; ++kk) {
 #pragma unroll
       for (int kb = 0; kb < kBN / 32; ++kb) {
-        bf16x8 a = *reinterpret_cast<const bf16x8*>(ks + (32 * kb + i) * KSTR + 16 * kk + 8 * h);
+        const int off = addr(32 * kb, 32 * kk) - addr(0, 0);
+        bf16x8 a = *(const __attribute__((address_space(3))) bf16x8*)(kt + kbase + off);
         s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, f.v[kk], s[kb], 0, 0, 0);
       }
     }
   }
 
-  // O^T += V^T P^T.  pk[ks] holds P for keys 16*ks .. 16*ks+15 of the tile as the B operand
-  // (bf16, in S^T register order).
-  __device__ static void accumulate(f32x16 (&o)[D / 32], const u32x4 (&pk)[kBN / 16], const uint16_t* vt, int lane) {
-    const int i = lane & 31, h = lane >> 5;
+  // O^T += V^T P^T; pk[ks] holds P for keys 16 ks .. 16 ks + 15 (S^T register order).
+  __device__ static void accumulate(f32x16 (&o)[D / 32], const u32x4 (&pk)[kBN / 16], const lds_char* vt, int vbase) {
+    typedef short s16x4 __attribute__((ext_vector_type(4)));
+    typedef short s16x8 __attribute__((ext_vector_type(8)));
+    typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+    const lds_char* vb = vt + vbase;
 #pragma unroll
     for (int ks = 0; ks < kBN / 16; ++ks) {
       const bf16x8 pb = __builtin_bit_cast(bf16x8, pk[ks]);
+      const int kb = ks >> 1, sh = ks & 1;
 #pragma unroll
       for (int db = 0; db < D / 32; ++db) {
-        bf16x8 a = *reinterpret_cast<const bf16x8*>(vt + (32 * db + i) * VSTR + 16 * ks + 8 * h);
-        o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb, o[db], 0, 0, 0);
+        const int off0 = addr(32 * kb + 16 * sh, 64 * db) - addr(0, 0);
+        const int off1 = addr(32 * kb + 16 * sh + 8, 64 * db) - addr(0, 0);
+        s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vb + off0));
+        s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vb + off1));
+        s16x8 a = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+        o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a), pb, o[db], 0, 0, 0);
       }
     }
   }
 
-  // Four consecutive output elements (d0..d0+3) of one row.
   __device__ static void store_out4(void* out, int64_t off, float a, float b, float c, float d) {
     u32x2 w = {pack_bf16x2(a, b), pack_bf16x2(c, d)};
     *reinterpret_cast<u32x2*>(reinterpret_cast<uint16_t*>(out) + off) = w;
@@ -501,23 +523,25 @@ struct Softmax {
   }
 };
 
-// bf16 path, software pipelined.  At the top of iteration j the scores S_j are
-// in registers, K_{j+1} and V_j are in LDS and K_{j+2}, V_{j+1} are in staging
-// registers.  Iteration j issues S_{j+1} = K_{j+1} Q^T on the MFMA pipe while
-// the exponentials of tile j run on the VALU, stages K_{j+2} and V_{j+1} into
-// the LDS buffers freed by the previous iteration, starts the global loads of
-// K_{j+3} and V_{j+2}, and accumulates O += V_j P_j.  One barrier per tile.
+
+// bf16 path with direct-to-LDS tiles.  At the top of iteration j the scores
+// S_j are in registers and K_{j+1}, V_j are in LDS.  Iteration j starts the
+// DMA of K_{j+2} and V_{j+1} into the buffers the previous iteration released,
+// issues S_{j+1} = K_{j+1} Q^T on the MFMA pipe while the exponentials of tile
+// j run on the VALU, accumulates O += V_j P_j, then waits for its DMA and
+// meets the other waves at the one barrier of the iteration.
 template <int D, bool PARTIAL>
-__device__ __forceinline__ void bf16_fwd_pipelined(const FwdArgs& a, char* smem) {
-  using P = Bf16Path<D>;
-  constexpr int K_ELEMS = kBN * P::KSTR, V_ELEMS = D * P::VSTR;
-  uint16_t* const kbuf0 = reinterpret_cast<uint16_t*>(smem);
-  uint16_t* const kbuf1 = kbuf0 + K_ELEMS;
-  uint16_t* const vbuf0 = kbuf1 + K_ELEMS;
-  uint16_t* const vbuf1 = vbuf0 + V_ELEMS;
+__device__ __forceinline__ void bf16_fwd_dma(const FwdArgs& a, char* smem_generic) {
+  using P = Bf16Dma<D>;
+  lds_char* const smem = (lds_char*)smem_generic;
+  lds_char* const kbuf0 = smem;
+  lds_char* const kbuf1 = smem + P::TILE_BYTES;
+  lds_char* const vbuf0 = smem + 2 * P::TILE_BYTES;
+  lds_char* const vbuf1 = smem + 3 * P::TILE_BYTES;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
+  const int wave_u = __builtin_amdgcn_readfirstlane(wave);
   const int h_half = lane >> 5;
   const Work w = decode<PARTIAL>(a, lane, wave);
   if (w.hi <= w.lo) {
@@ -530,13 +554,12 @@ __device__ __forceinline__ void bf16_fwd_pipelined(const FwdArgs& a, char* smem)
     const int r = nkeys - t * kBN;
     return r < 0 ? 0 : (r > kBN ? kBN : r);
   };
-
   const uint16_t* qrow = reinterpret_cast<const uint16_t*>(a.q) + (w.bh * a.Tq + (w.row_ok ? w.row : 0)) * D;
-  const uint16_t* kb = reinterpret_cast<const uint16_t*>(a.k) + (w.bh * a.S + w.lo) * D;
-  const uint16_t* vb = reinterpret_cast<const uint16_t*>(a.v) + (w.bh * a.S + w.lo) * D;
+  const uint16_t* kg = reinterpret_cast<const uint16_t*>(a.k) + (w.bh * a.S + w.lo) * D;
+  const uint16_t* vg = reinterpret_cast<const uint16_t*>(a.v) + (w.bh * a.S + w.lo) * D;
   // resource over the valid rows of tile t only (nothing past n_b is ever addressable)
-  auto k_tile = [&](int t) { return make_rsrc(kb + (int64_t)t * kBN * D, (uint32_t)nv_of(t) * (D * 2)); };
-  auto v_tile = [&](int t) { return make_rsrc(vb + (int64_t)t * kBN * D, (uint32_t)nv_of(t) * (D * 2)); };
+  auto k_tile = [&](int t) { return make_rsrc(kg + (int64_t)t * kBN * D, (uint32_t)nv_of(t) * (D * 2)); };
+  auto v_tile = [&](int t) { return make_rsrc(vg + (int64_t)t * kBN * D, (uint32_t)nv_of(t) * (D * 2)); };
 
   typename P::QFrag qf;
   P::load_q(qf, qrow, w.row_ok, h_half);
@@ -549,20 +572,17 @@ __device__ __forceinline__ void bf16_fwd_pipelined(const FwdArgs& a, char* smem)
       qf.v[kk] = __builtin_bit_cast(bf16x8, x);
     }
   }
+  const int kbase = P::k_base(lane);
+  const int vbase = P::v_base(lane);
 
-  u32x4 sk[P::NCH], sv[P::KPT];
-  P::load_k(sk, k_tile(0), tid);
-  P::load_v(sv, v_tile(0), tid);
-  P::store_k(sk, kbuf0, tid);
-  P::store_v(sv, vbuf0, tid);
-  P::load_k(sk, k_tile(1), tid);
-  P::load_v(sv, v_tile(1), tid);
+  P::dma_tile(k_tile(0), kbuf0, wave_u, lane);
+  P::dma_tile(v_tile(0), vbuf0, wave_u, lane);
+  P::dma_tile(k_tile(1), kbuf1, wave_u, lane);
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's tile loads have landed in LDS
   __syncthreads();
   f32x16 s_cur[kBN / 32];
-  P::scores(s_cur, qf, kbuf0, lane);
-  P::store_k(sk, kbuf1, tid);
-  P::load_k(sk, k_tile(2), tid);
-  __syncthreads();
+  P::scores(s_cur, qf, kbuf0, kbase);
+  __syncthreads();  // every wave is done with K_0 before its buffer is refilled
 
   f32x16 o[D / 32];
 #pragma unroll
@@ -571,19 +591,18 @@ __device__ __forceinline__ void bf16_fwd_pipelined(const FwdArgs& a, char* smem)
   u32x4 pk[kBN / 16];
 
   for (int j = 0; j < T - 1; ++j) {
-    uint16_t* const k_next = (j & 1) ? kbuf0 : kbuf1;  // K_{j+1}
-    uint16_t* const k_free = (j & 1) ? kbuf1 : kbuf0;  // K_j consumed -> K_{j+2}
-    uint16_t* const v_cur = (j & 1) ? vbuf1 : vbuf0;   // V_j
-    uint16_t* const v_free = (j & 1) ? vbuf0 : vbuf1;  // V_{j-1} consumed -> V_{j+1}
+    lds_char* const k_next = (j & 1) ? kbuf0 : kbuf1;  // K_{j+1}
+    lds_char* const k_free = (j & 1) ? kbuf1 : kbuf0;  // K_j consumed -> K_{j+2}
+    lds_char* const v_cur = (j & 1) ? vbuf1 : vbuf0;   // V_j
+    lds_char* const v_free = (j & 1) ? vbuf0 : vbuf1;  // V_{j-1} consumed -> V_{j+1}
+    P::dma_tile(k_tile(j + 2), k_free, wave_u, lane);
+    P::dma_tile(v_tile(j + 1), v_free, wave_u, lane);
     sm.update_max(s_cur, c, o);
     f32x16 s_next[kBN / 32];
-    P::scores(s_next, qf, k_next, lane);
+    P::scores(s_next, qf, k_next, kbase);
     sm.template exp_pack<false>(s_cur, c, pk, kBN, h_half);
-    P::store_v(sv, v_free, tid);
-    P::store_k(sk, k_free, tid);
-    P::load_v(sv, v_tile(j + 2), tid);
-    P::load_k(sk, k_tile(j + 3), tid);
-    P::accumulate(o, pk, v_cur, lane);
+    P::accumulate(o, pk, v_cur, vbase);
+    __builtin_amdgcn_s_waitcnt(0x0F70);
     __syncthreads();
 #pragma unroll
     for (int kb2 = 0; kb2 < kBN / 32; ++kb2) s_cur[kb2] = s_next[kb2];
@@ -600,7 +619,7 @@ __device__ __forceinline__ void bf16_fwd_pipelined(const FwdArgs& a, char* smem)
   }
   sm.update_max(s_cur, c, o);
   sm.template exp_pack<true>(s_cur, c, pk, nv_last, h_half);
-  P::accumulate(o, pk, ((T - 1) & 1) ? vbuf1 : vbuf0, lane);
+  P::accumulate(o, pk, ((T - 1) & 1) ? vbuf1 : vbuf0, vbase);
 
   const float l = pair_sum(sm.l);
   write_rows<P, D, PARTIAL>(a, w, o, 1.0f / l, (sm.m + __builtin_amdgcn_logf(l)) * kLn2, h_half);
@@ -613,8 +632,8 @@ void attn_fwd_kernel(FwdArgs a) {
     __shared__ __attribute__((aligned(16))) char smem[P::LDS_BYTES];
     attn_fwd_body<P, D, PARTIAL>(a, smem);
   } else {
-    __shared__ __attribute__((aligned(16))) char smem[2 * P::LDS_BYTES];
-    bf16_fwd_pipelined<D, PARTIAL>(a, smem);
+    __shared__ __attribute__((aligned(16))) char smem[P::LDS_BYTES];
+    bf16_fwd_dma<D, PARTIAL>(a, smem);
   }
 }
 
