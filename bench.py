@@ -84,7 +84,7 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--no-splitkv", action="store_true", help="skip the split-KV workload")
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle timing and parity sample")
-    ap.add_argument("--cpu-rows", type=int, default=64, help="oracle query rows per head for the CPU baseline")
+    ap.add_argument("--cpu-rows", type=int, default=1024, help="oracle query rows per head for the CPU baseline")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run one 1 GiB device copy (reference kernel for HBM counter scaling)")
     args = ap.parse_args()
@@ -130,7 +130,7 @@ def main() -> int:
     roofline = {
         "bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
         "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": traffic,
-        "kernel": "attn_fwd_kernel<Bf16Path<256>>", "avg_launch_ms": round(ms_avg, 4),
+        "kernel": "attn_fwd_kernel<Bf16Dma<256>>", "avg_launch_ms": round(ms_avg, 4),
         "algorithmic_flop_per_launch": flops,
     }
 

@@ -173,15 +173,20 @@ struct Bf16Dma {
 
   // Issue this wave's share of one tile's DMA (blocks wave, wave+4, ...).  The resource
   // covers only the tile's valid rows; other lanes write zeros without a fetch.
-  __device__ static void dma_tile(__amdgpu_buffer_rsrc_t rs, lds_char* buf, int wave_u, int lane) {
+  static constexpr int DMA_PER_WAVE = NBLK / 4;  // blocks of one tile each wave copies
+
+  // One block (the bi-th of this wave's share) of a tile.
+  __device__ static void dma_block(__amdgpu_buffer_rsrc_t rs, lds_char* buf, int wave_u, int lane, int bi) {
     const int r = lane / LPR, ch = lane % LPR;
+    const int b = wave_u + 4 * bi;
+    const int j = key_of(b, r);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void*)(buf + b * BLK), 16,
+                                             j * ROWB + ch * 16, 0, 0, 0);
+  }
+
+  __device__ static void dma_tile(__amdgpu_buffer_rsrc_t rs, lds_char* buf, int wave_u, int lane) {
 #pragma unroll
-    for (int bi = 0; bi < NBLK / 4; ++bi) {
-      const int b = wave_u + 4 * bi;
-      const int j = key_of(b, r);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void*)(buf + b * BLK), 16,
-                                               j * ROWB + ch * 16, 0, 0, 0);
-    }
+    for (int bi = 0; bi < DMA_PER_WAVE; ++bi) dma_block(rs, buf, wave_u, lane, bi);
   }
 
   // per-lane base of the QK^T operand read (key i = lane % 32 of block kb = 0, chunk h)
@@ -233,6 +238,24 @@ struct Bf16Dma {
   __device__ static void store_out4(void* out, int64_t off, float a, float b, float c, float d) {
     u32x2 w = {pack_bf16x2(a, b), pack_bf16x2(c, d)};
     *reinterpret_cast<u32x2*>(reinterpret_cast<uint16_t*>(out) + off) = w;
+  }
+  // ---- manually ordered iteration halves (sched_barrier fences pin the order) ----
+  __device__ static bf16x8 k_frag(const lds_char* kt, int kbase, int i) {
+    const int off = addr(32 * (i & 1), 32 * (i >> 1)) - addr(0, 0);
+    return *(const __attribute__((address_space(3))) bf16x8*)(kt + kbase + off);
+  }
+  __device__ static bf16x8 v_frag(const lds_char* vt, int vbase, int i) {
+    typedef short s16x4 __attribute__((ext_vector_type(4)));
+    typedef short s16x8 __attribute__((ext_vector_type(8)));
+    typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+    const int ks = i / (D / 32), db = i % (D / 32);
+    const int kb = ks >> 1, sh = ks & 1;
+    const int off0 = addr(32 * kb + 16 * sh, 64 * db) - addr(0, 0);
+    const int off1 = addr(32 * kb + 16 * sh + 8, 64 * db) - addr(0, 0);
+    s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vt + vbase + off0));
+    s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vt + vbase + off1));
+    s16x8 a = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    return __builtin_bit_cast(bf16x8, a);
   }
 };
 
@@ -478,16 +501,21 @@ struct Softmax {
   float m = -__builtin_inff();  // scaled log2-domain max the probabilities are taken against
   float l = 0.0f;               // this lane's partial row sum (lanes l and l^32 are added at the end)
 
-  // Row max of raw scores s (rows keys of this lane), rescale if it moved too far.
-  __device__ __forceinline__ void update_max(const f32x16 (&s)[kBN / 32], float c, f32x16 (&o)[D / 32]) {
+  // Scaled row max of raw scores s (this lane's keys, then its partner lane's).
+  __device__ __forceinline__ static float row_max(const f32x16 (&s)[kBN / 32], float c) {
     float mt = fmaxf(s[0][0], s[0][1]);
 #pragma unroll
     for (int kb = 0; kb < kBN / 32; ++kb)
 #pragma unroll
       for (int r = (kb == 0 ? 2 : 0); r < 16; ++r) mt = fmaxf(mt, s[kb][r]);
-    mt = pair_max(mt) * c;
+    return pair_max(mt) * c;
+  }
+
+  // Take a tile's scaled max into account: move m (and rescale O, l) only when the tile
+  // exceeds it by more than kRescaleLog2.  The branch is wave-uniform and rare.
+  __device__ __forceinline__ void apply_max(float mt, f32x16 (&o)[D / 32]) {
     const bool need = mt > m + kRescaleLog2;
-    if (__builtin_amdgcn_ballot_w64(need) != 0) {  // wave-uniform and rare
+    if (__builtin_amdgcn_ballot_w64(need) != 0) {
       const float m_new = fmaxf(m, mt);
       const float alpha = __builtin_amdgcn_exp2f(m - m_new);
       m = m_new;
@@ -525,14 +553,26 @@ struct Softmax {
 
 
 // bf16 path with direct-to-LDS tiles.  At the top of iteration j the scores
-// S_j are in registers and K_{j+1}, V_j are in LDS.  Iteration j starts the
-// DMA of K_{j+2} and V_{j+1} into the buffers the previous iteration released,
-// issues S_{j+1} = K_{j+1} Q^T on the MFMA pipe while the exponentials of tile
-// j run on the VALU, accumulates O += V_j P_j, then waits for its DMA and
-// meets the other waves at the one barrier of the iteration.
+// S_j are in registers, the running max already covers them, and K_{j+1}, V_j
+// are in LDS.  Iteration j starts the DMA of K_{j+2} and V_{j+1} into the
+// buffers the previous iteration released, issues S_{j+1} = K_{j+1} Q^T on the
+// MFMA pipe while the exponentials of tile j run on the VALU, accumulates
+// O += V_j P_j while the VALU takes the row max of S_{j+1}, then waits for its
+// DMA and meets the other waves at the one barrier of the iteration.  The last
+// tile, whose keys may be masked, takes its max after the loop.
+//
+// With one wave per SIMD (D = 256) no other wave hides stalls, so the
+// iteration is written as fixed slots -- one MFMA, the LDS operand read for
+// the MFMA kRing slots later, one element of softmax work and, in the first
+// slots, one block of the next tiles' DMA -- separated by sched_barrier fences
+// that keep the compiler from regrouping them.  With two waves per SIMD the
+// hardware interleaves the waves and the compiler's own order is used.
+constexpr int kRing = 2;  // LDS operand reads issued this many slots ahead (measured best)
+
 template <int D, bool PARTIAL>
 __device__ __forceinline__ void bf16_fwd_dma(const FwdArgs& a, char* smem_generic) {
   using P = Bf16Dma<D>;
+  constexpr bool kManual = (D == 256);
   lds_char* const smem = (lds_char*)smem_generic;
   lds_char* const kbuf0 = smem;
   lds_char* const kbuf1 = smem + P::TILE_BYTES;
@@ -589,35 +629,99 @@ __device__ __forceinline__ void bf16_fwd_dma(const FwdArgs& a, char* smem_generi
   for (int db = 0; db < D / 32; ++db) o[db] = f32x16{};
   Softmax<D> sm;
   u32x4 pk[kBN / 16];
+  if (T >= 2) sm.apply_max(Softmax<D>::row_max(s_cur, c), o);  // tile 0 is full when more follow
 
-  for (int j = 0; j < T - 1; ++j) {
+  auto iteration = [&](int j, auto next_max_tag) {
+    constexpr bool NEXT_MAX = decltype(next_max_tag)::value;  // take S_{j+1}'s max here
     lds_char* const k_next = (j & 1) ? kbuf0 : kbuf1;  // K_{j+1}
     lds_char* const k_free = (j & 1) ? kbuf1 : kbuf0;  // K_j consumed -> K_{j+2}
     lds_char* const v_cur = (j & 1) ? vbuf1 : vbuf0;   // V_j
     lds_char* const v_free = (j & 1) ? vbuf0 : vbuf1;  // V_{j-1} consumed -> V_{j+1}
-    P::dma_tile(k_tile(j + 2), k_free, wave_u, lane);
-    P::dma_tile(v_tile(j + 1), v_free, wave_u, lane);
-    sm.update_max(s_cur, c, o);
+    const __amdgpu_buffer_rsrc_t k_rs = k_tile(j + 2), v_rs = v_tile(j + 1);
+    if constexpr (!kManual) {
+      P::dma_tile(k_rs, k_free, wave_u, lane);
+      P::dma_tile(v_rs, v_free, wave_u, lane);
+    }
     f32x16 s_next[kBN / 32];
-    P::scores(s_next, qf, k_next, kbase);
-    sm.template exp_pack<false>(s_cur, c, pk, kBN, h_half);
-    P::accumulate(o, pk, v_cur, vbase);
+#pragma unroll
+    for (int kb = 0; kb < kBN / 32; ++kb) s_next[kb] = f32x16{};
+    if constexpr (kManual) {
+      constexpr int R = kRing;
+      constexpr int NS = P::NQ * (kBN / 32);     // QK^T MFMAs per tile
+      constexpr int NV = (D / 32) * (kBN / 16);  // PV MFMAs per tile
+      constexpr int EPS = (kBN / 2) / NS;        // softmax elements per QK^T slot
+      constexpr int MPS = (kBN / 2) / NV;        // max elements per PV slot
+      bf16x8 kf[R], vf[R];
+#pragma unroll
+      for (int i = 0; i < R; ++i) kf[i] = P::k_frag(k_next, kbase, i);
+      const float nm = -sm.m;
+      float acc[4] = {0.f, 0.f, 0.f, 0.f};
+      float pe[kBN / 2];
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int i = 0; i < NS; ++i) {
+        const int kb = i % (kBN / 32), kk = i / (kBN / 32);
+        s_next[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[i % R], qf.v[kk], s_next[kb], 0, 0, 0);
+        if (i + R < NS) kf[i % R] = P::k_frag(k_next, kbase, i + R);
+        if (i >= NS - R) vf[i - (NS - R)] = P::v_frag(v_cur, vbase, i - (NS - R));
+        // the tile DMA is spread one block per slot over the first QK^T slots: all of it at
+        // once would hold this wave's in-order issue (and the MFMA pipe) behind the loads
+        if (i < 2 * P::DMA_PER_WAVE) {
+          if (i < P::DMA_PER_WAVE) P::dma_block(k_rs, k_free, wave_u, lane, i);
+          else P::dma_block(v_rs, v_free, wave_u, lane, i - P::DMA_PER_WAVE);
+        }
+#pragma unroll
+        for (int t = 0; t < EPS; ++t) {
+          const int e = i * EPS + t;  // register e % 16 of S^T block e / 16
+          const float x = __builtin_amdgcn_exp2f(__builtin_fmaf(s_cur[e >> 4][e & 15], c, nm));
+          pe[e] = x;
+          acc[e & 3] += x;
+          if (e & 1) pk[e >> 3][(e & 7) >> 1] = pack_bf16x2(pe[e - 1], x);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      sm.l += (acc[0] + acc[1]) + (acc[2] + acc[3]);
+      float mx = -__builtin_inff();
+#pragma unroll
+      for (int i = 0; i < NV; ++i) {
+        const int ks = i / (D / 32), db = i % (D / 32);
+        o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[i % R], __builtin_bit_cast(bf16x8, pk[ks]), o[db], 0, 0, 0);
+        if (i + R < NV) vf[i % R] = P::v_frag(v_cur, vbase, i + R);
+        if constexpr (NEXT_MAX) {
+#pragma unroll
+          for (int t = 0; t < MPS; ++t) {
+            const int e = i * MPS + t;
+            mx = fmaxf(mx, s_next[e >> 4][e & 15]);
+          }
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      if constexpr (NEXT_MAX) sm.apply_max(pair_max(mx) * c, o);
+    } else {
+      P::scores(s_next, qf, k_next, kbase);
+      sm.template exp_pack<false>(s_cur, c, pk, kBN, h_half);
+      P::accumulate(o, pk, v_cur, vbase);
+      if constexpr (NEXT_MAX) sm.apply_max(Softmax<D>::row_max(s_next, c), o);
+    }
     __builtin_amdgcn_s_waitcnt(0x0F70);
     __syncthreads();
 #pragma unroll
-    for (int kb2 = 0; kb2 < kBN / 32; ++kb2) s_cur[kb2] = s_next[kb2];
-  }
+    for (int kb = 0; kb < kBN / 32; ++kb) s_cur[kb] = s_next[kb];
+  };
 
-  // last tile: S_{T-1} in s_cur, V_{T-1} in vbuf[(T-1) & 1]; mask keys >= nv
+  for (int j = 0; j < T - 2; ++j) iteration(j, std::true_type{});
+  if (T >= 2) iteration(T - 2, std::false_type{});
+
+  // last tile: S_{T-1} in s_cur, V_{T-1} in vbuf[(T-1) & 1]; keys >= nv are masked
   const int nv_last = nv_of(T - 1);
   if (nv_last < kBN) {
 #pragma unroll
-    for (int kb2 = 0; kb2 < kBN / 32; ++kb2)
+    for (int kb = 0; kb < kBN / 32; ++kb)
 #pragma unroll
       for (int r = 0; r < 16; ++r)
-        if (st_key(kb2, r, h_half) >= nv_last) s_cur[kb2][r] = -__builtin_inff();
+        if (st_key(kb, r, h_half) >= nv_last) s_cur[kb][r] = -__builtin_inff();
   }
-  sm.update_max(s_cur, c, o);
+  sm.apply_max(Softmax<D>::row_max(s_cur, c), o);
   sm.template exp_pack<true>(s_cur, c, pk, nv_last, h_half);
   P::accumulate(o, pk, ((T - 1) & 1) ? vbuf1 : vbuf0, vbase);
 
