@@ -175,13 +175,21 @@ struct Bf16Dma {
   // covers only the tile's valid rows; other lanes write zeros without a fetch.
   static constexpr int DMA_PER_WAVE = NBLK / 4;  // blocks of one tile each wave copies
 
-  // One block (the bi-th of this wave's share) of a tile.
+  // One block (the bi-th of this wave's share) of a tile.  Issued as inline asm on
+  // purpose: the compiler cannot tell which LDS bytes a direct-to-LDS load writes,
+  // so for the builtin it waits for every such load in flight before any later LDS
+  // read (stalling each iteration on the next tile's loads).  Here the kernel
+  // orders these loads itself: an explicit vmcnt wait and an LDS barrier come
+  // before any read of a buffer they fill, and a buffer being filled is never
+  // read in the same iteration.  M0 holds the LDS destination.
   __device__ static void dma_block(__amdgpu_buffer_rsrc_t rs, lds_char* buf, int wave_u, int lane, int bi) {
     const int r = lane / LPR, ch = lane % LPR;
     const int b = wave_u + 4 * bi;
     const int j = key_of(b, r);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void*)(buf + b * BLK), 16,
-                                             j * ROWB + ch * 16, 0, 0, 0);
+    const uint32_t lds = (uint32_t)(uintptr_t)(buf + b * BLK);
+    const uint32_t voff = (uint32_t)(j * ROWB + ch * 16);
+    asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds" ::"s"(lds), "v"(voff), "s"(rs)
+                 : "m0");
   }
 
   __device__ static void dma_tile(__amdgpu_buffer_rsrc_t rs, lds_char* buf, int wave_u, int lane) {
@@ -488,6 +496,14 @@ __device__ __forceinline__ void attn_fwd_body(const FwdArgs& a, char* smem) {
   write_rows<P, D, PARTIAL>(a, w, o, 1.0f / l, (m + __builtin_amdgcn_logf(l)) * kLn2, h_half);
 }
 
+// Workgroup barrier that orders LDS only: tile loads in flight (vmcnt) are not
+// drained, so callers wait for exactly the loads they need before it.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
 // Online-softmax state of one lane (one query row, half of its keys).  The
 // running max m is kept in the scaled log2 domain and is moved only when a
 // tile's max exceeds it by more than kRescaleLog2: probabilities are computed
@@ -567,7 +583,7 @@ struct Softmax {
 // slots, one block of the next tiles' DMA -- separated by sched_barrier fences
 // that keep the compiler from regrouping them.  With two waves per SIMD the
 // hardware interleaves the waves and the compiler's own order is used.
-constexpr int kRing = 2;  // LDS operand reads issued this many slots ahead (measured best)
+constexpr int kRing = 2;  // LDS operand reads issued this many slots ahead (2..4 measure the same)
 
 template <int D, bool PARTIAL>
 __device__ __forceinline__ void bf16_fwd_dma(const FwdArgs& a, char* smem_generic) {
@@ -703,14 +719,15 @@ __device__ __forceinline__ void bf16_fwd_dma(const FwdArgs& a, char* smem_generi
       P::accumulate(o, pk, v_cur, vbase);
       if constexpr (NEXT_MAX) sm.apply_max(Softmax<D>::row_max(s_next, c), o);
     }
-    __builtin_amdgcn_s_waitcnt(0x0F70);
-    __syncthreads();
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this iteration's tile loads have landed
+    lds_barrier();
 #pragma unroll
     for (int kb = 0; kb < kBN / 32; ++kb) s_cur[kb] = s_next[kb];
   };
 
   for (int j = 0; j < T - 2; ++j) iteration(j, std::true_type{});
   if (T >= 2) iteration(T - 2, std::false_type{});
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // no tile load may still be writing LDS when the workgroup ends
 
   // last tile: S_{T-1} in s_cur, V_{T-1} in vbuf[(T-1) & 1]; keys >= nv are masked
   const int nv_last = nv_of(T - 1);
