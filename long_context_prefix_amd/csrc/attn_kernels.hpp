@@ -647,7 +647,9 @@ __device__ __forceinline__ void bf16_fwd_dma(const FwdArgs& a, char* smem_generi
   u32x4 pk[kBN / 16];
   if (T >= 2) sm.apply_max(Softmax<D>::row_max(s_cur, c), o);  // tile 0 is full when more follow
 
-  auto iteration = [&](int j, auto next_max_tag) {
+  // sc holds S_j; S_{j+1} is accumulated into sn (two register sets, used alternately, so that
+  // no MFMA of one iteration has to wait for the reads of the previous iteration's scores)
+  auto iteration = [&](int j, auto next_max_tag, f32x16 (&sc)[kBN / 32], f32x16 (&sn)[kBN / 32]) {
     constexpr bool NEXT_MAX = decltype(next_max_tag)::value;  // take S_{j+1}'s max here
     lds_char* const k_next = (j & 1) ? kbuf0 : kbuf1;  // K_{j+1}
     lds_char* const k_free = (j & 1) ? kbuf1 : kbuf0;  // K_j consumed -> K_{j+2}
@@ -658,9 +660,8 @@ __device__ __forceinline__ void bf16_fwd_dma(const FwdArgs& a, char* smem_generi
       P::dma_tile(k_rs, k_free, wave_u, lane);
       P::dma_tile(v_rs, v_free, wave_u, lane);
     }
-    f32x16 s_next[kBN / 32];
 #pragma unroll
-    for (int kb = 0; kb < kBN / 32; ++kb) s_next[kb] = f32x16{};
+    for (int kb = 0; kb < kBN / 32; ++kb) sn[kb] = f32x16{};
     if constexpr (kManual) {
       constexpr int R = kRing;
       constexpr int NS = P::NQ * (kBN / 32);     // QK^T MFMAs per tile
@@ -677,7 +678,7 @@ __device__ __forceinline__ void bf16_fwd_dma(const FwdArgs& a, char* smem_generi
 #pragma unroll
       for (int i = 0; i < NS; ++i) {
         const int kb = i % (kBN / 32), kk = i / (kBN / 32);
-        s_next[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[i % R], qf.v[kk], s_next[kb], 0, 0, 0);
+        sn[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[i % R], qf.v[kk], sn[kb], 0, 0, 0);
         if (i + R < NS) kf[i % R] = P::k_frag(k_next, kbase, i + R);
         if (i >= NS - R) vf[i - (NS - R)] = P::v_frag(v_cur, vbase, i - (NS - R));
         // the tile DMA is spread one block per slot over the first QK^T slots: all of it at
@@ -689,7 +690,7 @@ __device__ __forceinline__ void bf16_fwd_dma(const FwdArgs& a, char* smem_generi
 #pragma unroll
         for (int t = 0; t < EPS; ++t) {
           const int e = i * EPS + t;  // register e % 16 of S^T block e / 16
-          const float x = __builtin_amdgcn_exp2f(__builtin_fmaf(s_cur[e >> 4][e & 15], c, nm));
+          const float x = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[e >> 4][e & 15], c, nm));
           pe[e] = x;
           acc[e & 3] += x;
           if (e & 1) pk[e >> 3][(e & 7) >> 1] = pack_bf16x2(pe[e - 1], x);
@@ -707,26 +708,49 @@ __device__ __forceinline__ void bf16_fwd_dma(const FwdArgs& a, char* smem_generi
 #pragma unroll
           for (int t = 0; t < MPS; ++t) {
             const int e = i * MPS + t;
-            mx = fmaxf(mx, s_next[e >> 4][e & 15]);
+            mx = fmaxf(mx, sn[e >> 4][e & 15]);
           }
         }
         __builtin_amdgcn_sched_barrier(0);
       }
       if constexpr (NEXT_MAX) sm.apply_max(pair_max(mx) * c, o);
     } else {
-      P::scores(s_next, qf, k_next, kbase);
-      sm.template exp_pack<false>(s_cur, c, pk, kBN, h_half);
+      P::scores(sn, qf, k_next, kbase);
+      sm.template exp_pack<false>(sc, c, pk, kBN, h_half);
       P::accumulate(o, pk, v_cur, vbase);
-      if constexpr (NEXT_MAX) sm.apply_max(Softmax<D>::row_max(s_next, c), o);
+      if constexpr (NEXT_MAX) sm.apply_max(Softmax<D>::row_max(sn, c), o);
     }
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this iteration's tile loads have landed
     lds_barrier();
-#pragma unroll
-    for (int kb = 0; kb < kBN / 32; ++kb) s_cur[kb] = s_next[kb];
   };
 
-  for (int j = 0; j < T - 2; ++j) iteration(j, std::true_type{});
-  if (T >= 2) iteration(T - 2, std::false_type{});
+  f32x16 s_alt[kBN / 32];
+  if constexpr (kManual) {
+    int j = 0;
+    for (; j + 1 < T - 2; j += 2) {
+      iteration(j, std::true_type{}, s_cur, s_alt);
+      iteration(j + 1, std::true_type{}, s_alt, s_cur);
+    }
+    if (j < T - 2) {  // one more full iteration, then the last one
+      iteration(j, std::true_type{}, s_cur, s_alt);
+      iteration(j + 1, std::false_type{}, s_alt, s_cur);
+    } else if (T >= 2) {
+      iteration(T - 2, std::false_type{}, s_cur, s_alt);
+#pragma unroll
+      for (int kb = 0; kb < kBN / 32; ++kb) s_cur[kb] = s_alt[kb];
+    }
+  } else {
+    for (int j = 0; j < T - 2; ++j) {
+      iteration(j, std::true_type{}, s_cur, s_alt);
+#pragma unroll
+      for (int kb = 0; kb < kBN / 32; ++kb) s_cur[kb] = s_alt[kb];
+    }
+    if (T >= 2) {  // the last tile may be masked: its max is taken after the loop
+      iteration(T - 2, std::false_type{}, s_cur, s_alt);
+#pragma unroll
+      for (int kb = 0; kb < kBN / 32; ++kb) s_cur[kb] = s_alt[kb];
+    }
+  }
   __builtin_amdgcn_s_waitcnt(0x0F70);  // no tile load may still be writing LDS when the workgroup ends
 
   // last tile: S_{T-1} in s_cur, V_{T-1} in vbuf[(T-1) & 1]; keys >= nv are masked
