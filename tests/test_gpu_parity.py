@@ -241,3 +241,79 @@ def test_no_device_allocation():
     free1, _ = torch.cuda.mem_get_info()
     assert torch.cuda.memory_allocated() == alloc0
     assert free1 == free0
+
+
+@pytest.mark.parametrize("D", [64, 256])
+def test_splitkv_other_head_dims(D):
+    B, H, Tq, S = 2, 2, 140, 700
+    lens = [650, 0]
+    log(f"splitkv D={D}")
+    q, k, v, kv = make_inputs(B, H, Tq, S, D, lens, "bf16", 1.0, seed=1200 + D, device=DEV)
+    scale = 1.0 / math.sqrt(D)
+    po, pl = _lib.attn_splitkv_partial(q, k, v, kv, 256, scale)
+    torch.cuda.synchronize()
+    rpo, rpl = ref_splitkv_partial(_np(q), _np(k), _np(v), np.array(lens), scale, 256)
+    assert_parity(po, pl, rpo, rpl, "bf16", f"partials D={D}")
+    out, lse = _lib.splitkv_fwd(q, k, v, kv, 256, scale)
+    torch.cuda.synchronize()
+    ro, rl = _oracle(q, k, v, kv, scale)
+    assert_parity(out, lse, ro, rl, "bf16", f"split end-to-end D={D}")
+
+
+@pytest.mark.parametrize("scale", [-0.0625, 0.0, 0.9])
+def test_scale_sign_and_zero(scale):
+    """Negative scales (Q is negated internally), scale 0 (uniform weights) and a large scale."""
+    D, B, H, Tq, S = 256, 2, 2, 130, 300
+    lens = [300, 77]
+    q, k, v, kv = make_inputs(B, H, Tq, S, D, lens, "bf16", 1.0, seed=1300, device=DEV)
+    out, lse = _run_fused(q, k, v, kv, scale)
+    ro, rl = _oracle(q, k, v, kv, scale)
+    assert_parity(out, lse, ro, rl, "bf16", f"scale={scale}")
+    po, pl = _lib.attn_splitkv_partial(q, k, v, kv, 64, scale)
+    so, sl = _lib.attn_lse_combine(po, pl, torch.float32)
+    torch.cuda.synchronize()
+    assert_parity(so, sl, ro, rl, "bf16", f"split scale={scale}")
+
+
+@pytest.mark.parametrize("D", [128, 256])
+def test_growing_scores_exercise_rescale(D):
+    """Key norms grow along the sequence, so the running max keeps moving past the lazy
+    rescale threshold and O is rescaled many times inside one row."""
+    B, H, Tq, S = 1, 2, 64, 2048
+    g = torch.Generator(device=DEV).manual_seed(1400 + D)
+    q = torch.randn(B, H, Tq, D, device=DEV, generator=g).abs().to(torch.bfloat16)
+    ramp = torch.linspace(0.0, 6.0, S, device=DEV).view(1, 1, S, 1)
+    k = (torch.rand(B, H, S, D, device=DEV, generator=g) * ramp).to(torch.bfloat16)
+    v = torch.randn(B, H, S, D, device=DEV, generator=g).to(torch.bfloat16)
+    kv = torch.tensor([S], dtype=torch.int32, device=DEV)
+    scale = 1.0 / math.sqrt(D)
+    out, lse = _run_fused(q, k, v, kv, scale)
+    ro, rl = _oracle(q, k, v, kv, scale)
+    assert np.isfinite(rl).all() and rl.max() > 20.0  # scores grow far past the 2^8 rescale threshold
+    assert_parity(out, lse, ro, rl, "bf16", f"growing D={D}")
+
+
+@pytest.mark.timeout(900)
+def test_largest_key_slice():
+    """One (b, h) key slice just under the 2^31-byte limit (D=256 bf16, S = 2^22 - 64):
+    offsets near the top of the range stay correct."""
+    D, S = 256, (1 << 22) - 64
+    n = S - 5
+    Tq = 64
+    g = torch.Generator(device=DEV).manual_seed(1500)
+    k = torch.empty(1, 1, S, D, dtype=torch.bfloat16, device=DEV)
+    v = torch.empty_like(k)
+    k.normal_(generator=g)
+    v.normal_(generator=g)
+    q = torch.randn(1, 1, Tq, D, device=DEV, generator=g).to(torch.bfloat16)
+    kv = torch.tensor([n], dtype=torch.int32, device=DEV)
+    out, lse = _run_fused(q, k, v, kv, 0.0625)
+    # the oracle over all n keys, on 16 query rows
+    rows = torch.arange(0, Tq, 4, device=DEV)
+    ro, rl = ref_prefix_fwd(_np(q[:, :, rows]), _np(k[:, :, :n]), _np(v[:, :, :n]), [n], 0.0625)
+    assert_parity(out[:, :, rows], lse[:, :, rows], ro, rl, "bf16", "largest slice")
+    # the tail keys matter: a query aligned with the last valid key sees it dominate
+    q2 = (k[:, :, n - 1:n] * 8).contiguous()
+    o2, l2 = _run_fused(q2, k, v, kv, 0.0625)
+    r2o, r2l = ref_prefix_fwd(_np(q2), _np(k[:, :, :n]), _np(v[:, :, :n]), [n], 0.0625)
+    assert_parity(o2, l2, r2o, r2l, "bf16", "largest slice, last key")
