@@ -45,6 +45,7 @@ import math
 import numpy as np
 
 __all__ = [
+    "ref_prefix_mask_to_kv_len",
     "scale64",
     "ref_prefix_fwd",
     "ref_splitkv_partial",
@@ -181,6 +182,28 @@ def ref_lse_combine(part_out, part_lse, axis: int = 2):
     out = np.where(empty[..., None], 0.0, out)
     lse = np.where(empty, -np.inf, m_safe + np.log(wsum_safe))
     return out, lse
+
+
+def ref_prefix_mask_to_kv_len(mask):
+    """Lengths of prefix key-padding masks, or -1 for rows that are not prefixes.
+
+    The page on tabfm PR #80 (section Fix) rewrites a boolean key mask only when its
+    valid keys are exactly the first n rows; PR #81 (section cuDNN flash attention)
+    maps such masks onto one length per batch element.  mask: [B, S] or [B, 1, 1, S]
+    booleans, True = attend.  Row b gives n_b = the number of leading True entries if
+    every later entry is False, and -1 otherwise (a hole, or a True after a False).
+    An all-False row is a valid prefix of length 0.
+    """
+    m = np.asarray(mask).astype(bool)
+    m = m.reshape(m.shape[0], -1)
+    out = np.empty(m.shape[0], dtype=np.int64)
+    for b in range(m.shape[0]):
+        row = m[b].tolist()
+        n = 0
+        while n < len(row) and row[n]:
+            n += 1
+        out[b] = n if not any(row[n:]) else -1
+    return out
 
 
 def brute_force(q, k, v, kv_len, scale: float):

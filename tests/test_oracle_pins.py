@@ -439,3 +439,47 @@ def test_planted_mistakes_are_caught(mutant, monkeypatch):
         except (AssertionError, ValueError):
             failures += 1
     assert failures >= 1, f"planted mistake {mutant!r} passed every pin"
+
+
+# ------------------------------------------------------------- mask -> lengths
+
+
+def test_mask_to_kv_len_hand_cases():
+    from oracle import ref_prefix_mask_to_kv_len as f
+
+    T, F = True, False
+    cases = [
+        ([T, T, T, T], 4),  # all valid
+        ([F, F, F, F], 0),  # all-False mask: a legal prefix of length 0 (PR #80, Tests)
+        ([T, T, F, F], 2),
+        ([T, F, F, F], 1),
+        ([T, F, T, F], -1),  # a hole: not a prefix mask
+        ([F, T, T, T], -1),  # suffix mask
+        ([T, T, T, F, T], -1),
+    ]
+    for row, n in cases:
+        assert f(np.array([row]))[0] == n, (row, n)
+    # [B,1,1,S] layout, ragged lengths, and S = 0
+    m = np.zeros((3, 1, 1, 6), dtype=bool)
+    m[0, ..., :6] = True
+    m[1, ..., :1] = True
+    assert f(m).tolist() == [6, 1, 0]
+    assert f(np.zeros((2, 0), dtype=bool)).tolist() == [0, 0]
+
+
+def test_mask_lengths_feed_the_truncation_identity():
+    """For prefix masks, masked attention (torch, float64) equals the oracle at the derived lengths."""
+    from oracle import ref_prefix_mask_to_kv_len
+
+    rng = np.random.default_rng(21)
+    B, H, tq, S, d = 4, 2, 5, 30, 8
+    lens = np.array([30, 1, 17, 9])
+    mask = np.arange(S)[None, :] < lens[:, None]
+    got = ref_prefix_mask_to_kv_len(mask[:, None, None, :])
+    assert got.tolist() == lens.tolist()
+    q, k, v = (rng.standard_normal((B, H, n, d)) for n in (tq, S, S))
+    out, _ = ref_prefix_fwd(q, k, v, got, 0.3)
+    ref = torch.nn.functional.scaled_dot_product_attention(
+        torch.from_numpy(q), torch.from_numpy(k), torch.from_numpy(v),
+        attn_mask=torch.from_numpy(mask[:, None, None, :]), scale=float(np.float32(0.3)))
+    np.testing.assert_allclose(out, ref.numpy(), rtol=0, atol=1e-12)
