@@ -118,6 +118,23 @@ attn_status_t attn_splitkv_partial(const void* q, const void* k, const void* v, 
 attn_status_t attn_lse_combine(const float* part_out, const float* part_lse, int B, int H, int C, int Tq,
                                int D, attn_dtype_t out_dtype, void* out, float* lse, void* stream);
 
+/* Prefix-mask detection on the device: the step before a masked attention call
+ * that the page on tabfm PR #80 (section Fix) performs on the host, and the
+ * mask-to-sequence-lengths mapping of PR #81 (section cuDNN flash attention).
+ *   mask       : device, B rows of S bytes (nonzero = attend); row b starts at
+ *                mask + b * row_stride (bytes, row_stride >= 0; 0 repeats one row
+ *                for every b); a [B,1,1,S] bool tensor is such a layout.  NULL is
+ *                allowed when S = 0 (every row is then the empty prefix, n_b = 0).
+ *   kv_len     : device int32 [B]; receives n_b when row b is True...True
+ *                False...False (n_b = number of True entries, 0 for an all-False
+ *                row) and -1 when the row is not a prefix mask.  A -1 must not
+ *                reach the attention calls (they would clamp it to 0): callers
+ *                check for it, which needs one host synchronization.
+ * Errors: ATTN_ERR_SHAPE (negative B, S or row_stride), ATTN_ERR_NULLPTR,
+ * ATTN_ERR_ALIGN (kv_len not 4-byte aligned), ATTN_ERR_HIP.  B = 0 is a no-op. */
+attn_status_t attn_prefix_mask_to_kv_len(const uint8_t* mask, int B, int S, int64_t row_stride, int32_t* kv_len,
+                                         void* stream);
+
 /* Host helper: number of chunks ceil(S / chunk); -1 if chunk <= 0 or S < 0. */
 int attn_splitkv_num_chunks(int S, int chunk);
 

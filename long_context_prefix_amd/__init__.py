@@ -6,7 +6,10 @@ The public calls mirror the C ABI of ``libattnprefix.so``:
   element b attends only to its first ``kv_len[b]`` keys;
 * ``attn_splitkv_partial(q, k, v, kv_len, chunk, scale)`` -- fp32 partials
   over fixed key chunks;
-* ``attn_lse_combine(part_out, part_lse)`` -- their exact log-sum-exp merge.
+* ``attn_lse_combine(part_out, part_lse)`` -- their exact log-sum-exp merge;
+* ``attn_prefix_mask_to_kv_len(mask)`` / ``sdpa_prefix(q, k, v, attn_mask)`` --
+  a [B, 1, 1, S] boolean prefix mask turned into lengths on the device, and an
+  SDPA-style entry that raises on any other mask.
 
 The library is loaded on first use; a missing build raises instead of falling
 back to anything else.
@@ -16,9 +19,12 @@ from ._lib import (  # noqa: F401
     AttnError,
     attn_lse_combine,
     attn_prefix_fwd,
+    attn_prefix_mask_to_kv_len,
     attn_splitkv_num_chunks,
     attn_splitkv_partial,
+    kv_len_from_prefix_mask,
     load,
+    sdpa_prefix,
     splitkv_fwd,
     status_string,
 )

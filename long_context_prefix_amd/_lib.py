@@ -24,7 +24,7 @@ STATUS_NAMES = {
 }
 ATTN_BF16, ATTN_F32 = 0, 1
 EXPORTED = ("attn_version", "attn_prefix_fwd", "attn_splitkv_partial", "attn_lse_combine",
-            "attn_splitkv_num_chunks", "attn_status_string")
+            "attn_prefix_mask_to_kv_len", "attn_splitkv_num_chunks", "attn_status_string")
 
 _lib = None
 
@@ -53,6 +53,8 @@ def load() -> ctypes.CDLL:
     L.attn_splitkv_partial.argtypes = [vp, vp, vp, vp, i32, i32, i32, i32, i32, f32, i32, i32, vp, vp, vp]
     L.attn_lse_combine.restype = i32
     L.attn_lse_combine.argtypes = [vp, vp, i32, i32, i32, i32, i32, i32, vp, vp, vp]
+    L.attn_prefix_mask_to_kv_len.restype = i32
+    L.attn_prefix_mask_to_kv_len.argtypes = [vp, i32, i32, ctypes.c_int64, vp, vp]
     L.attn_splitkv_num_chunks.restype = i32
     L.attn_splitkv_num_chunks.argtypes = [i32, i32]
     L.attn_status_string.restype = ctypes.c_char_p
@@ -189,3 +191,53 @@ def splitkv_fwd(q, k, v, kv_len, chunk: int, scale: Optional[float] = None, retu
     """Split-KV attention: per-chunk partials, then the exact merge (two launches, one stream)."""
     po, pl = attn_splitkv_partial(q, k, v, kv_len, chunk, scale)
     return attn_lse_combine(po, pl, q.dtype, return_lse=return_lse)
+
+
+def attn_prefix_mask_to_kv_len(mask: torch.Tensor, kv_len: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Device-side conversion of a key mask ([B, S] or [B, 1, 1, S], bool or uint8,
+    True = attend) into int32 lengths; a row that is not a prefix mask gives -1."""
+    if mask.dim() == 4:
+        if mask.shape[1] != 1 or mask.shape[2] != 1:
+            raise ValueError("a 4-D key mask must be [B, 1, 1, S] (broadcast over heads and queries)")
+        B, S = mask.shape[0], mask.shape[3]
+        row_stride = mask.stride(0)
+    elif mask.dim() == 2:
+        B, S = mask.shape
+        row_stride = mask.stride(0)
+    else:
+        raise ValueError("key mask must be [B, S] or [B, 1, 1, S]")
+    if mask.dtype not in (torch.bool, torch.uint8):
+        raise ValueError("key mask must be bool or uint8 (a float bias is not a padding mask)")
+    if mask.device.type != "cuda":
+        raise ValueError("mask must live on a GPU")
+    if row_stride < 0:
+        raise ValueError("negative batch stride")
+    if S > 1 and mask.stride(-1) != 1:
+        raise ValueError("the key axis of the mask must be contiguous")
+    if kv_len is None:
+        kv_len = torch.empty(B, dtype=torch.int32, device=mask.device)
+    elif kv_len.dtype != torch.int32 or kv_len.shape != (B,) or kv_len.device != mask.device:
+        raise ValueError("kv_len must be int32 [B] on the mask's device")
+    code = load().attn_prefix_mask_to_kv_len(_ptr(mask), B, S, int(row_stride), _ptr(kv_len),
+                                             _stream(mask.device))
+    _check("attn_prefix_mask_to_kv_len", code)
+    return kv_len
+
+
+def kv_len_from_prefix_mask(mask: torch.Tensor) -> torch.Tensor:
+    """Lengths of a prefix key-padding mask; raises ValueError (after one sync) for any
+    row that is not True...True False...False.  There is no fallback to a dense mask."""
+    kv_len = attn_prefix_mask_to_kv_len(mask)
+    bad = torch.nonzero(kv_len < 0).flatten()
+    if bad.numel():
+        raise ValueError(f"attention mask rows {bad.tolist()[:8]} are not prefix key-padding masks")
+    return kv_len
+
+
+def sdpa_prefix(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, attn_mask: torch.Tensor,
+                scale: Optional[float] = None) -> torch.Tensor:
+    """Scaled-dot-product attention with a [B, 1, 1, S] (or [B, S]) boolean prefix key mask,
+    ragged lengths included, on the fused kernel.  Non-prefix masks raise."""
+    kv_len = kv_len_from_prefix_mask(attn_mask)
+    out, _ = attn_prefix_fwd(q, k, v, kv_len, scale, return_lse=False)
+    return out

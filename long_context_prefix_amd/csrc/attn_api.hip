@@ -91,6 +91,19 @@ extern "C" {
 
 int attn_version(void) { return (0 << 16) | (1 << 8) | 0; }
 
+attn_status_t attn_prefix_mask_to_kv_len(const uint8_t* mask, int B, int S, int64_t row_stride, int32_t* kv_len,
+                                         void* stream) {
+  if (B < 0 || S < 0 || row_stride < 0) return ATTN_ERR_SHAPE;
+  if (B == 0) return ATTN_OK;
+  if (!kv_len || (S > 0 && !mask)) return ATTN_ERR_NULLPTR;
+  if (!aligned4(kv_len)) return ATTN_ERR_ALIGN;
+  if (verbose()) fprintf(stderr, "[attn_prefix] prefix_mask_to_kv_len B=%d S=%d\n", B, S);
+  (void)hipGetLastError();
+  hipLaunchKernelGGL(prefix_mask_kernel, dim3((unsigned)B), dim3(kMaskThreads), 0,
+                     reinterpret_cast<hipStream_t>(stream), mask, S, row_stride, kv_len);
+  return hipGetLastError() == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
+}
+
 int attn_splitkv_num_chunks(int S, int chunk) {
   if (chunk <= 0 || S < 0) return -1;
   return (int)(((int64_t)S + chunk - 1) / chunk);

@@ -845,4 +845,70 @@ void lse_combine_kernel(CombineArgs a) {
   if (a.lse && col == 0) a.lse[row] = (mx == -__builtin_inff()) ? mx : mx + __builtin_amdgcn_logf(wsum) * kLn2;
 }
 
+// ------------------------------------------------------- prefix mask -> kv_len
+// One workgroup per batch row of a boolean key mask (one byte per key, nonzero =
+// attend).  The row is a prefix mask exactly when its last nonzero byte comes
+// before its first zero byte; then n_b = index of the first zero (S if none),
+// otherwise -1.  This is the detection the page on tabfm PR #80 (section Fix)
+// performs before rewriting a mask into a truncation, done on the device so the
+// attention launch needs no host round trip for the lengths.  The row body is
+// read as aligned 16-byte vectors; the unaligned head and the tail (under 16
+// bytes each) are read bytewise by the first 32 lanes.
+constexpr int kMaskThreads = 512;
+
+// bit i set <=> byte i of w is nonzero (the carry of (b & 0x7f) + 0x7f stays in the byte)
+__device__ __forceinline__ unsigned nonzero_bytes4(unsigned w) {
+  const unsigned t = (((w & 0x7f7f7f7fu) + 0x7f7f7f7fu) | w) & 0x80808080u;
+  return ((t >> 7) & 1u) | ((t >> 14) & 2u) | ((t >> 21) & 4u) | ((t >> 28) & 8u);
+}
+
+__global__ __launch_bounds__(kMaskThreads)
+void prefix_mask_kernel(const uint8_t* mask, int S, int64_t row_stride, int32_t* kv_len) {
+  const uint8_t* row = mask + (int64_t)blockIdx.x * row_stride;
+  const int t = threadIdx.x;
+  int first_zero = S, last_one = -1;
+  const int mis = (int)(reinterpret_cast<uintptr_t>(row) & 15);
+  const int head = min(S, (16 - mis) & 15);
+  const int nvec = (S - head) >> 4;
+  const int tail0 = head + (nvec << 4);
+  if (t < 32) {
+    const int j = t < 16 ? t : tail0 + (t - 16);
+    if (j < (t < 16 ? head : S)) {
+      if (row[j]) last_one = j;
+      else first_zero = j;
+    }
+  }
+  const uint4* vec = reinterpret_cast<const uint4*>(row + head);
+  for (int i = t; i < nvec; i += kMaskThreads) {
+    const uint4 w = vec[i];
+    const unsigned nz = nonzero_bytes4(w.x) | (nonzero_bytes4(w.y) << 4) | (nonzero_bytes4(w.z) << 8) |
+                        (nonzero_bytes4(w.w) << 12);
+    const int o = head + (i << 4);
+    if (nz) last_one = max(last_one, o + 31 - (int)__clz(nz));
+    const unsigned z = ~nz & 0xffffu;
+    if (z) first_zero = min(first_zero, o + __ffs(z) - 1);
+  }
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) {
+    first_zero = min(first_zero, __shfl_xor(first_zero, off));
+    last_one = max(last_one, __shfl_xor(last_one, off));
+  }
+  constexpr int kWaves = kMaskThreads / 64;
+  __shared__ int fz[kWaves], lo[kWaves];
+  if ((t & 63) == 0) {
+    fz[t >> 6] = first_zero;
+    lo[t >> 6] = last_one;
+  }
+  __syncthreads();
+  if (t == 0) {
+    int f = fz[0], l = lo[0];
+#pragma unroll
+    for (int w = 1; w < kWaves; ++w) {
+      f = min(f, fz[w]);
+      l = max(l, lo[w]);
+    }
+    kv_len[blockIdx.x] = (l < f) ? f : -1;
+  }
+}
+
 }  // namespace lcp

@@ -160,3 +160,28 @@ def test_missing_library_fails_loudly(monkeypatch, tmp_path):
     monkeypatch.setattr(_lib, "LIB_PATH", str(tmp_path / "absent.so"))
     with pytest.raises(ImportError):
         _lib.load()
+
+
+def test_mask_to_kv_len_argument_errors(L):
+    def call(mask=P, B=2, S=8, stride=8, kv=P):
+        return L.attn_prefix_mask_to_kv_len(mask, B, S, stride, kv, None)
+
+    assert call(B=-1) == SHAPE
+    assert call(S=-1) == SHAPE
+    assert call(stride=-8) == SHAPE
+    assert call(mask=None) == NULLPTR
+    assert call(kv=None) == NULLPTR
+    assert call(kv=ctypes.c_void_p(4098)) == ALIGN
+    assert call(B=0, mask=None, kv=None) == OK  # empty batch: nothing launched
+
+
+def test_mask_binding_rejects_bad_masks():
+    m = torch.ones(2, 1, 1, 8, dtype=torch.bool)
+    with pytest.raises(ValueError):
+        _lib.attn_prefix_mask_to_kv_len(m)  # CPU tensor
+    with pytest.raises(ValueError):
+        _lib.attn_prefix_mask_to_kv_len(torch.ones(2, 2, 1, 8, dtype=torch.bool))  # per-head mask
+    with pytest.raises(ValueError):
+        _lib.attn_prefix_mask_to_kv_len(torch.zeros(2, 8, dtype=torch.float32))  # additive bias
+    with pytest.raises(ValueError):
+        _lib.attn_prefix_mask_to_kv_len(torch.ones(8, dtype=torch.bool))
