@@ -181,14 +181,17 @@ struct Bf16Dma {
   // read (stalling each iteration on the next tile's loads).  Here the kernel
   // orders these loads itself: an explicit vmcnt wait and an LDS barrier come
   // before any read of a buffer they fill, and a buffer being filled is never
-  // read in the same iteration.  M0 holds the LDS destination.
+  // read in the same iteration.  M0 holds the LDS destination; an LDS-DMA load
+  // needs one wait state after the SALU write of M0 (the s_nop).  Nothing else in
+  // these kernels uses M0.
   __device__ static void dma_block(__amdgpu_buffer_rsrc_t rs, lds_char* buf, int wave_u, int lane, int bi) {
     const int r = lane / LPR, ch = lane % LPR;
     const int b = wave_u + 4 * bi;
     const int j = key_of(b, r);
     const uint32_t lds = (uint32_t)(uintptr_t)(buf + b * BLK);
     const uint32_t voff = (uint32_t)(j * ROWB + ch * 16);
-    asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds" ::"s"(lds), "v"(voff), "s"(rs)
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds" ::"s"(lds), "v"(voff),
+                 "s"(rs)
                  : "m0");
   }
 
@@ -496,6 +499,20 @@ __device__ __forceinline__ void attn_fwd_body(const FwdArgs& a, char* smem) {
   write_rows<P, D, PARTIAL>(a, w, o, 1.0f / l, (m + __builtin_amdgcn_logf(l)) * kLn2, h_half);
 }
 
+// S^T accumulation with the accumulator in VGPRs.  With one wave per SIMD the
+// compiler gives every MFMA the AGPR form, which would make each score travel
+// AGPR -> VGPR (v_accvgpr_read) before the softmax can touch it; written out here
+// the score MFMAs keep their result where the VALU reads it, while the O
+// accumulator stays in AGPRs.  Because the compiler does not know these are
+// MFMAs, their consumers must leave the wait states the hardware requires
+// between an XDL result and a VALU read (the fixed-slot schedule below does).
+__device__ __forceinline__ void mfma_vgpr_first(f32x16& d, bf16x8 a, bf16x8 b) {
+  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(d) : "v"(a), "v"(b));
+}
+__device__ __forceinline__ void mfma_vgpr_acc(f32x16& d, bf16x8 a, bf16x8 b) {
+  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(d) : "v"(a), "v"(b));
+}
+
 // Workgroup barrier that orders LDS only: tile loads in flight (vmcnt) are not
 // drained, so callers wait for exactly the loads they need before it.
 __device__ __forceinline__ void lds_barrier() {
@@ -637,7 +654,19 @@ __device__ __forceinline__ void bf16_fwd_dma(const FwdArgs& a, char* smem_generi
   __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's tile loads have landed in LDS
   __syncthreads();
   f32x16 s_cur[kBN / 32];
-  P::scores(s_cur, qf, kbuf0, kbase);
+  if constexpr (kManual) {  // same register form as the loop's score MFMAs
+#pragma unroll
+    for (int kk = 0; kk < P::NQ; ++kk)
+#pragma unroll
+      for (int kb = 0; kb < kBN / 32; ++kb) {
+        const bf16x8 kf = P::k_frag(kbuf0, kbase, (kBN / 32) * kk + kb);
+        if (kk == 0) mfma_vgpr_first(s_cur[kb], kf, qf.v[0]);
+        else mfma_vgpr_acc(s_cur[kb], kf, qf.v[kk]);
+      }
+    asm volatile("s_nop 7\n\ts_nop 7" ::: "memory");  // XDL result -> VALU read (row_max below)
+  } else {
+    P::scores(s_cur, qf, kbuf0, kbase);
+  }
   __syncthreads();  // every wave is done with K_0 before its buffer is refilled
 
   f32x16 o[D / 32];
@@ -660,8 +689,10 @@ __device__ __forceinline__ void bf16_fwd_dma(const FwdArgs& a, char* smem_generi
       P::dma_tile(k_rs, k_free, wave_u, lane);
       P::dma_tile(v_rs, v_free, wave_u, lane);
     }
+    if constexpr (!kManual) {
 #pragma unroll
-    for (int kb = 0; kb < kBN / 32; ++kb) sn[kb] = f32x16{};
+      for (int kb = 0; kb < kBN / 32; ++kb) sn[kb] = f32x16{};
+    }
     if constexpr (kManual) {
       constexpr int R = kRing;
       constexpr int NS = P::NQ * (kBN / 32);     // QK^T MFMAs per tile
@@ -678,7 +709,8 @@ __device__ __forceinline__ void bf16_fwd_dma(const FwdArgs& a, char* smem_generi
 #pragma unroll
       for (int i = 0; i < NS; ++i) {
         const int kb = i % (kBN / 32), kk = i / (kBN / 32);
-        sn[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[i % R], qf.v[kk], sn[kb], 0, 0, 0);
+        if (kk == 0) mfma_vgpr_first(sn[kb], kf[i % R], qf.v[0]);
+        else mfma_vgpr_acc(sn[kb], kf[i % R], qf.v[kk]);
         if (i + R < NS) kf[i % R] = P::k_frag(k_next, kbase, i + R);
         if (i >= NS - R) vf[i - (NS - R)] = P::v_frag(v_cur, vbase, i - (NS - R));
         // the tile DMA is spread one block per slot over the first QK^T slots: all of it at
@@ -698,6 +730,11 @@ __device__ __forceinline__ void bf16_fwd_dma(const FwdArgs& a, char* smem_generi
         __builtin_amdgcn_sched_barrier(0);
       }
       sm.l += (acc[0] + acc[1]) + (acc[2] + acc[3]);
+      // the scores were written by MFMAs the compiler does not see as such: keep the
+      // VALU reads of S_{j+1} below clear of the last of them (16 wait states here,
+      // on top of the two MFMA issues in between)
+      asm volatile("s_nop 7\n\ts_nop 7" ::: "memory");
+      __builtin_amdgcn_sched_barrier(0);
       float mx = -__builtin_inff();
 #pragma unroll
       for (int i = 0; i < NV; ++i) {
