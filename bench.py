@@ -77,6 +77,29 @@ def time_launches(fn, steps: int, torch):
     return wall, [s.elapsed_time(e) for s, e in evs]
 
 
+def fetch_scaling(torch, _lib) -> int:
+    """Fused launches at B=1, H=8, D=128, Tq=128 (one query tile per head, so each valid
+    key row is fetched once) over S=131072 slots whose padded rows hold +-1e4, with
+    n = S, S/2 and S/4.  Under a FETCH_SIZE counter run the bytes per dispatch should
+    scale with n (2 * n * D * 2 bytes of K/V per head), showing that padded slots are
+    never read."""
+    from long_context_prefix_amd.workloads import make_inputs
+
+    B, H, Tq, S, D = 1, 8, 128, 131072, 128
+    res = []
+    for n in (S, S // 2, S // 4):
+        q, k, v, kv = make_inputs(B, H, Tq, S, D, [n], "bf16", 1.0, seed=4242, device="cuda")
+        out = torch.empty_like(q)
+        for _ in range(3):
+            _lib.attn_prefix_fwd(q, k, v, kv, 1.0 / D ** 0.5, out=out)
+        torch.cuda.synchronize()
+        res.append({"n": n, "valid_kv_bytes_per_launch": 2 * H * n * D * 2, "launches": 3})
+        log(f"fetch scaling: n={n} done")
+        del q, k, v, out
+    print(json.dumps({"fetch_scaling": res, "B": B, "H": H, "T_q": Tq, "S": S, "head_dim": D}), flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -84,9 +107,12 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--no-splitkv", action="store_true", help="skip the split-KV workload")
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle timing and parity sample")
-    ap.add_argument("--cpu-rows", type=int, default=1024, help="oracle query rows per head for the CPU baseline")
+    ap.add_argument("--cpu-rows", type=int, default=4096, help="oracle query rows per head for the CPU baseline")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run one 1 GiB device copy (reference kernel for HBM counter scaling)")
+    ap.add_argument("--fetch-scaling", action="store_true",
+                    help="only run the fused kernel on one query tile per head over S=131072 slots with "
+                         "n = S, S/2, S/4 (for HBM fetch counters: bytes read must follow n, not S)")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -103,6 +129,8 @@ def main() -> int:
     _lib.load()  # fails loudly when the HIP library is missing
     torch.cuda.set_device(0)
     src_hash = kernel_source_hash()
+    if args.fetch_scaling:
+        return fetch_scaling(torch, _lib)
 
     # ------------------------------------------------------------- fused path
     w = WORKLOADS["icl_121k"]
