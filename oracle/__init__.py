@@ -8,6 +8,7 @@ from .attn_oracle import (  # noqa: F401
     brute_force,
     num_chunks,
     ref_lse_combine,
+    ref_prefix_bwd,
     ref_prefix_mask_to_kv_len,
     ref_prefix_fwd,
     ref_splitkv_partial,

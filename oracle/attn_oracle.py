@@ -32,7 +32,11 @@ Readings where the pages are silent (each is listed in the design notes):
 * n = 0 (an all-False mask row) gives out = 0 and lse = -inf, and so does an
   empty chunk and a merge in which every partial is -inf;
 * ``scale`` is rounded to fp32 first, because the kernels receive an fp32;
-* every query row is valid (no causal mask) and T_q is independent of S.
+* every query row is valid (no causal mask) and T_q is independent of S;
+* the backward pass (gradients for training on ragged, packed batches) is the
+  exact derivative of the forward above with respect to q, k and v; padded key
+  slots do not enter the function, so their gradient is exactly zero, and a row
+  block with n = 0 (constant output 0) has zero gradients everywhere.
 
 Parity pins for every function live in ``tests/test_oracle_pins.py``; none of
 the functions here is "parity unpinned".
@@ -45,6 +49,7 @@ import math
 import numpy as np
 
 __all__ = [
+    "ref_prefix_bwd",
     "ref_prefix_mask_to_kv_len",
     "scale64",
     "ref_prefix_fwd",
@@ -182,6 +187,66 @@ def ref_lse_combine(part_out, part_lse, axis: int = 2):
     out = np.where(empty[..., None], 0.0, out)
     lse = np.where(empty, -np.inf, m_safe + np.log(wsum_safe))
     return out, lse
+
+
+def _grad_one(q: np.ndarray, k: np.ndarray, v: np.ndarray, dout: np.ndarray, s64: float):
+    """Gradients of out = softmax(s64 * q k^T) v for one (b, h), keys already truncated.
+
+    Plain definition, in query-row blocks (dk and dv sum over the blocks):
+        P = softmax(s64 q k^T) ; dv = P^T dout ; dP = dout v^T
+        delta = rowsum(P * dP)  (equal to rowsum(dout * out))
+        dS = P * (dP - delta) ; dq = s64 dS k ; dk = s64 dS^T q
+    With n == 0 every gradient is zero.
+    """
+    t = q.shape[0]
+    n = k.shape[0]
+    dq = np.zeros_like(q)
+    dk = np.zeros_like(k)
+    dv = np.zeros_like(v)
+    if n == 0 or t == 0:
+        return dq, dk, dv
+    for r0 in range(0, t, _ROW_BLOCK):
+        r1 = min(t, r0 + _ROW_BLOCK)
+        scores = s64 * (q[r0:r1] @ k.T)
+        e = np.exp(scores - scores.max(axis=1, keepdims=True))
+        p = e / e.sum(axis=1, keepdims=True)
+        do = dout[r0:r1]
+        dv += p.T @ do
+        dp = do @ v.T
+        delta = (p * dp).sum(axis=1, keepdims=True)
+        ds = p * (dp - delta)
+        dq[r0:r1] = s64 * (ds @ k)
+        dk += s64 * (ds.T @ q[r0:r1])
+    return dq, dk, dv
+
+
+def ref_prefix_bwd(q, k, v, kv_len, scale: float, dout):
+    """Backward of the prefix-masked forward: returns (dq, dk, dv) in fp64.
+
+    Shapes as in ``ref_prefix_fwd``; dout is [B, H, T_q, D].  Keys are sliced to
+    their first n_b rows before any arithmetic, so dk and dv are exactly zero on
+    the padded slots j >= n_b whatever those slots hold (the truncation identity
+    of PR #80, section Fix, carried to the gradients).
+    """
+    q = _as64(q)
+    dout = _as64(dout)
+    b_, h_, t_, d_ = q.shape
+    kv_len = np.asarray(kv_len).reshape(-1)
+    assert kv_len.shape[0] == b_
+    s_slots = k.shape[2]
+    s64 = scale64(scale)
+    dq = np.zeros(q.shape, dtype=np.float64)
+    dk = np.zeros(k.shape, dtype=np.float64)
+    dv = np.zeros(v.shape, dtype=np.float64)
+    for b in range(b_):
+        n = int(kv_len[b])
+        assert 0 <= n <= s_slots
+        for h in range(h_):
+            gq, gk, gv = _grad_one(q[b, h], _as64(k[b, h, :n]), _as64(v[b, h, :n]), dout[b, h], s64)
+            dq[b, h] = gq
+            dk[b, h, :n] = gk
+            dv[b, h, :n] = gv
+    return dq, dk, dv
 
 
 def ref_prefix_mask_to_kv_len(mask):
