@@ -65,7 +65,7 @@ typedef enum {
   ATTN_ERR_NULLPTR = 1,      /* a required pointer is NULL */
   ATTN_ERR_SHAPE = 2,        /* a negative size, or a size beyond the limits above */
   ATTN_ERR_DTYPE = 3,        /* dtype is not one of attn_dtype_t */
-  ATTN_ERR_UNSUPPORTED = 4,  /* head dim D not in {64, 128, 256} */
+  ATTN_ERR_UNSUPPORTED = 4,  /* head dim or dtype not supported by this call */
   ATTN_ERR_ALIGN = 5,        /* a tensor pointer is not 16-byte aligned */
   ATTN_ERR_CHUNK = 6,        /* chunk <= 0 or not a multiple of 64 */
   ATTN_ERR_HIP = 7,          /* the HIP runtime reported an error at launch */
@@ -134,6 +134,29 @@ attn_status_t attn_lse_combine(const float* part_out, const float* part_lse, int
  * ATTN_ERR_ALIGN (kv_len not 4-byte aligned), ATTN_ERR_HIP.  B = 0 is a no-op. */
 attn_status_t attn_prefix_mask_to_kv_len(const uint8_t* mask, int B, int S, int64_t row_stride, int32_t* kv_len,
                                          void* stream);
+
+/* Backward pass of attn_prefix_fwd: the exact gradients of the same function,
+ * for training on packed batches whose elements have ragged prefix lengths
+ * (tabfm PR #80, section Fix, on the masked form at pretraining time; the
+ * truncation identity of the same section holds for the derivative too, so
+ * padded key slots get zero gradient).  With P = softmax(scale q k^T) over j < n_b, recomputed
+ * from `lse`:
+ *     delta_i = sum_d dout_id out_id,  dS = P * (dout v^T - delta)
+ *     dq = scale dS k,  dk = scale dS^T q,  dv = P^T dout
+ *   q, k, v, kv_len, scale : as passed to attn_prefix_fwd (same layouts)
+ *   out, lse   : that call's results (device; out [B,H,Tq,D] bf16, lse fp32)
+ *   dout       : device bf16 [B,H,Tq,D], the gradient of out
+ *   delta      : device fp32 [B,H,Tq], caller-provided workspace; receives delta
+ *   dq         : device bf16 [B,H,Tq,D]; dk, dv: device bf16 [B,H,S,D]; every
+ *                element is written (dk = dv = 0 on slots j >= n_b; dq = 0 for
+ *                batch elements with n_b = 0)
+ * Supported: dtype ATTN_BF16 with D in {64, 128} (other dtypes or head dims
+ * return ATTN_ERR_UNSUPPORTED).  Three kernels are enqueued on `stream`
+ * (delta, dq, dk/dv); no atomics, so results are deterministic.  Tq = 0 zeroes
+ * dk and dv; S = 0 zeroes dq. */
+attn_status_t attn_prefix_bwd(const void* q, const void* k, const void* v, const int32_t* kv_len, const void* out,
+                              const void* dout, const float* lse, int B, int H, int Tq, int S, int D, float scale,
+                              attn_dtype_t dtype, float* delta, void* dq, void* dk, void* dv, void* stream);
 
 /* Host helper: number of chunks ceil(S / chunk); -1 if chunk <= 0 or S < 0. */
 int attn_splitkv_num_chunks(int S, int chunk);

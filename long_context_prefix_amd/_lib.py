@@ -24,7 +24,7 @@ STATUS_NAMES = {
 }
 ATTN_BF16, ATTN_F32 = 0, 1
 EXPORTED = ("attn_version", "attn_prefix_fwd", "attn_splitkv_partial", "attn_lse_combine",
-            "attn_prefix_mask_to_kv_len", "attn_splitkv_num_chunks", "attn_status_string")
+            "attn_prefix_mask_to_kv_len", "attn_prefix_bwd", "attn_splitkv_num_chunks", "attn_status_string")
 
 _lib = None
 
@@ -55,6 +55,8 @@ def load() -> ctypes.CDLL:
     L.attn_lse_combine.argtypes = [vp, vp, i32, i32, i32, i32, i32, i32, vp, vp, vp]
     L.attn_prefix_mask_to_kv_len.restype = i32
     L.attn_prefix_mask_to_kv_len.argtypes = [vp, i32, i32, ctypes.c_int64, vp, vp]
+    L.attn_prefix_bwd.restype = i32
+    L.attn_prefix_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, f32, i32, vp, vp, vp, vp, vp]
     L.attn_splitkv_num_chunks.restype = i32
     L.attn_splitkv_num_chunks.argtypes = [i32, i32]
     L.attn_status_string.restype = ctypes.c_char_p
@@ -241,3 +243,59 @@ def sdpa_prefix(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, attn_mask: to
     kv_len = kv_len_from_prefix_mask(attn_mask)
     out, _ = attn_prefix_fwd(q, k, v, kv_len, scale, return_lse=False)
     return out
+
+
+def attn_prefix_bwd(q, k, v, kv_len, out, dout, lse, scale: Optional[float] = None,
+                    dq: Optional[torch.Tensor] = None, dk: Optional[torch.Tensor] = None,
+                    dv: Optional[torch.Tensor] = None, delta: Optional[torch.Tensor] = None):
+    """Gradients (dq, dk, dv) of the prefix-masked forward, bf16, D in {64, 128}.
+
+    ``out`` and ``lse`` are the forward's results; ``delta`` is an optional fp32
+    [B, H, Tq] workspace (rowsum(dout * out)).  dk and dv are zero on padded slots.
+    """
+    B, H, Tq, S, D, dev = _fwd_shapes(q, k, v, kv_len)
+    scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
+    for t, name in ((out, "out"), (dout, "dout")):
+        _require(t, name, dev)
+        if t.shape != q.shape or t.dtype != q.dtype:
+            raise ValueError(f"{name} must match q in shape and dtype")
+    _require(lse, "lse", dev)
+    if lse.shape != (B, H, Tq) or lse.dtype != torch.float32:
+        raise ValueError("lse must be fp32 [B, H, Tq]")
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    delta = torch.empty((B, H, Tq), dtype=torch.float32, device=dev) if delta is None else delta
+    for t, ref, name in ((dq, q, "dq"), (dk, k, "dk"), (dv, v, "dv")):
+        _require(t, name, dev)
+        if t.shape != ref.shape or t.dtype != ref.dtype:
+            raise ValueError(f"{name} has the wrong shape or dtype")
+    _require(delta, "delta", dev)
+    if delta.shape != (B, H, Tq) or delta.dtype != torch.float32:
+        raise ValueError("delta must be fp32 [B, H, Tq]")
+    code = load().attn_prefix_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(kv_len), _ptr(out), _ptr(dout), _ptr(lse),
+                                  B, H, Tq, S, D, scale, _dtype_code(q), _ptr(delta), _ptr(dq), _ptr(dk), _ptr(dv),
+                                  _stream(dev))
+    _check("attn_prefix_bwd", code)
+    return dq, dk, dv
+
+
+class _PrefixAttention(torch.autograd.Function):
+    @staticmethod
+    def forward(ctx, q, k, v, kv_len, scale):
+        out, lse = attn_prefix_fwd(q, k, v, kv_len, scale)
+        ctx.save_for_backward(q, k, v, kv_len, out, lse)
+        ctx.scale = scale
+        return out
+
+    @staticmethod
+    def backward(ctx, dout):
+        q, k, v, kv_len, out, lse = ctx.saved_tensors
+        dq, dk, dv = attn_prefix_bwd(q, k, v, kv_len, out, dout.contiguous(), lse, ctx.scale)
+        return dq, dk, dv, None, None
+
+
+def prefix_attention(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, kv_len: torch.Tensor,
+                     scale: Optional[float] = None) -> torch.Tensor:
+    """Differentiable prefix-masked attention (forward and backward on the HIP kernels)."""
+    return _PrefixAttention.apply(q, k, v, kv_len, scale)

@@ -6,6 +6,7 @@
 #include <stdio.h>
 #include <stdlib.h>
 
+#include "attn_bwd_kernels.hpp"
 #include "attn_kernels.hpp"
 #include "attn_prefix.h"
 
@@ -85,6 +86,24 @@ attn_status_t dispatch_fwd(const FwdArgs& a, int D, attn_dtype_t dtype, int64_t 
   return ATTN_ERR_UNSUPPORTED;
 }
 
+template <int D, int WPE_DQ, int WPE_DKDV>
+attn_status_t launch_bwd(const BwdArgs& base, int64_t rows, int64_t grid_dq, int64_t grid_dkdv, hipStream_t s) {
+  (void)hipGetLastError();
+  BwdArgs a = base;
+  if (rows > 0) {
+    constexpr int rows_per_wg = 256 / (D / 8);
+    const int64_t g = (rows + rows_per_wg - 1) / rows_per_wg;
+    hipLaunchKernelGGL((bwd_delta_kernel<D>), dim3((unsigned)g), dim3(256), 0, s, a, rows);
+    a.n_tiles = (a.Tq + kBM - 1) / kBM;
+    hipLaunchKernelGGL((bwd_dq_kernel<D, WPE_DQ>), dim3((unsigned)grid_dq), dim3(kThreads), 0, s, a);
+  }
+  if (grid_dkdv > 0) {
+    a.n_tiles = (a.S + 127) / 128;
+    hipLaunchKernelGGL((bwd_dkdv_kernel<D, WPE_DKDV>), dim3((unsigned)grid_dkdv), dim3(kThreads), 0, s, a);
+  }
+  return hipGetLastError() == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
+}
+
 }  // namespace
 
 extern "C" {
@@ -104,6 +123,55 @@ attn_status_t attn_prefix_mask_to_kv_len(const uint8_t* mask, int B, int S, int6
   return hipGetLastError() == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
 }
 
+attn_status_t attn_prefix_bwd(const void* q, const void* k, const void* v, const int32_t* kv_len, const void* out,
+                              const void* dout, const float* lse, int B, int H, int Tq, int S, int D, float scale,
+                              attn_dtype_t dtype, float* delta, void* dq, void* dk, void* dv, void* stream) {
+  if (dtype != ATTN_BF16 && dtype != ATTN_F32) return ATTN_ERR_DTYPE;
+  if (B < 0 || H < 0 || Tq < 0 || S < 0 || D < 0) return ATTN_ERR_SHAPE;
+  if (dtype != ATTN_BF16 || (D != 64 && D != 128)) return ATTN_ERR_UNSUPPORTED;
+  if (!isfinite(scale)) return ATTN_ERR_ARG;
+  if (B == 0 || H == 0 || (Tq == 0 && S == 0)) return ATTN_OK;
+  if (!kv_len) return ATTN_ERR_NULLPTR;
+  if (Tq > 0 && (!q || !out || !dout || !lse || !delta || !dq)) return ATTN_ERR_NULLPTR;
+  if (S > 0 && (!dk || !dv)) return ATTN_ERR_NULLPTR;
+  if (S > 0 && Tq > 0 && (!k || !v)) return ATTN_ERR_NULLPTR;
+  if (!aligned4(kv_len)) return ATTN_ERR_ALIGN;
+  if (Tq > 0 && (!aligned16(q) || !aligned16(out) || !aligned16(dout) || !aligned16(dq) || !aligned4(lse) ||
+                 !aligned4(delta)))
+    return ATTN_ERR_ALIGN;
+  if (S > 0 && (!aligned16(dk) || !aligned16(dv) || (Tq > 0 && (!aligned16(k) || !aligned16(v)))))
+    return ATTN_ERR_ALIGN;
+  if ((int64_t)S * D * 2 > kMaxI32) return ATTN_ERR_SHAPE;
+  const int64_t rows = (int64_t)B * H * Tq;
+  const int64_t grid_dq = (int64_t)B * H * ((Tq + kBM - 1) / kBM);
+  const int64_t grid_dkdv = (int64_t)B * H * (((int64_t)S + 127) / 128);
+  if (grid_dq > kMaxI32 || grid_dkdv > kMaxI32 || rows / (256 / (D / 8)) >= kMaxI32) return ATTN_ERR_SHAPE;
+  BwdArgs a{};
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.kv_len = kv_len;
+  a.out = out;
+  a.dout = dout;
+  a.lse = lse;
+  a.delta = delta;
+  a.B = B;
+  a.H = H;
+  a.Tq = Tq;
+  a.S = S;
+  a.scale = scale;
+  a.scale_log2 = scale * kLog2e;
+  a.dq = dq;
+  a.dk = dk;
+  a.dv = dv;
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  if (verbose())
+    fprintf(stderr, "[attn_prefix] prefix_bwd D=%d B=%d H=%d Tq=%d S=%d grid dq=%lld dkdv=%lld\n", D, B, H, Tq, S,
+            (long long)grid_dq, (long long)grid_dkdv);
+  if (D == 64) return launch_bwd<64, 2, 2>(a, rows, grid_dq, grid_dkdv, st);
+  return launch_bwd<128, 1, 1>(a, rows, grid_dq, grid_dkdv, st);
+}
+
 int attn_splitkv_num_chunks(int S, int chunk) {
   if (chunk <= 0 || S < 0) return -1;
   return (int)(((int64_t)S + chunk - 1) / chunk);
@@ -115,7 +183,8 @@ const char* attn_status_string(attn_status_t s) {
     case ATTN_ERR_NULLPTR: return "a required pointer is NULL";
     case ATTN_ERR_SHAPE: return "a size is negative or exceeds the library limits";
     case ATTN_ERR_DTYPE: return "unknown dtype (expected ATTN_BF16 or ATTN_F32)";
-    case ATTN_ERR_UNSUPPORTED: return "unsupported head dim (supported: 64, 128, 256)";
+    case ATTN_ERR_UNSUPPORTED:
+      return "unsupported head dim or dtype for this call (forward: D 64/128/256; backward: bf16, D 64/128)";
     case ATTN_ERR_ALIGN: return "a tensor pointer is misaligned (16 bytes required; 4 for kv_len and lse)";
     case ATTN_ERR_CHUNK: return "chunk must be a positive multiple of 64";
     case ATTN_ERR_HIP: return "the HIP runtime reported an error";

@@ -185,3 +185,25 @@ def test_mask_binding_rejects_bad_masks():
         _lib.attn_prefix_mask_to_kv_len(torch.zeros(2, 8, dtype=torch.float32))  # additive bias
     with pytest.raises(ValueError):
         _lib.attn_prefix_mask_to_kv_len(torch.ones(8, dtype=torch.bool))
+
+
+def test_bwd_argument_errors(L):
+    def call(q=P, k=P, v=P, kv=P, out=P, dout=P, lse=P, B=1, H=1, Tq=8, S=8, D=64, scale=0.125, dt=BF16,
+             delta=P, dq=P, dk=P, dv=P):
+        return L.attn_prefix_bwd(q, k, v, kv, out, dout, lse, B, H, Tq, S, D, scale, dt, delta, dq, dk, dv, None)
+
+    assert call(dt=9) == DTYPE
+    assert call(B=-1) == SHAPE
+    assert call(dt=F32) == UNSUP  # the backward is bf16 only
+    assert call(D=256) == UNSUP
+    assert call(D=32) == UNSUP
+    assert call(scale=float("nan")) == ARG
+    for name in ("q", "kv", "out", "dout", "lse", "delta", "dq", "dk", "dv", "k", "v"):
+        assert call(**{name: None}) == NULLPTR, name
+    for name in ("q", "out", "dout", "dq", "dk", "dv", "k", "v"):
+        assert call(**{name: PM}) == ALIGN, name
+    assert call(lse=ctypes.c_void_p(4097)) == ALIGN
+    assert call(delta=ctypes.c_void_p(4098)) == ALIGN
+    assert call(B=0, q=None, k=None, v=None, kv=None, out=None, dout=None, lse=None, delta=None, dq=None, dk=None,
+                dv=None) == OK
+    assert call(S=2**23, D=128) == SHAPE  # 2^31 bytes per (b, h) slice
