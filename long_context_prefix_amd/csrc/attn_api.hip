@@ -169,7 +169,7 @@ attn_status_t attn_prefix_bwd(const void* q, const void* k, const void* v, const
     fprintf(stderr, "[attn_prefix] prefix_bwd D=%d B=%d H=%d Tq=%d S=%d grid dq=%lld dkdv=%lld\n", D, B, H, Tq, S,
             (long long)grid_dq, (long long)grid_dkdv);
   if (D == 64) return launch_bwd<64, 2, 2>(a, rows, grid_dq, grid_dkdv, st);
-  return launch_bwd<128, 1, 1>(a, rows, grid_dq, grid_dkdv, st);
+  return launch_bwd<128, 2, 1>(a, rows, grid_dq, grid_dkdv, st);
 }
 
 int attn_splitkv_num_chunks(int S, int chunk) {

@@ -273,8 +273,9 @@ void bwd_dkdv_kernel(BwdArgs a) {
       next_stat = stat_load(t + 1);
     }
     f32x16 s[kBN / 32], dp[kBN / 32];
-    P::scores(s, kf, qb_(cur), kbase);   // S = Q K^T   (rows: queries of the tile, lane: key)
-    P::scores(dp, vf, gb_(cur), kbase);  // dP = dO V^T
+    P::scores_vgpr(s, kf, qb_(cur), kbase);   // S = Q K^T   (rows: queries of the tile, lane: key)
+    P::scores_vgpr(dp, vf, gb_(cur), kbase);  // dP = dO V^T
+    xdl_result_guard();
     u32x4 ppk[kBN / 16], dpk[kBN / 16];
 #pragma unroll
     for (int ks = 0; ks < kBN / 16; ++ks) {

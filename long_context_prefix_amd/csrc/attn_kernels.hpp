@@ -101,6 +101,28 @@ __device__ __forceinline__ u32x4 buf_load16(__amdgpu_buffer_rsrc_t rs, uint32_t 
   return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, (int)off, 0, 0));
 }
 
+// S^T accumulation with the accumulator in VGPRs.  With one wave per SIMD the
+// compiler gives every MFMA the AGPR form, which would make each score travel
+// AGPR -> VGPR (v_accvgpr_read) before the softmax can touch it; written out here
+// the score MFMAs keep their result where the VALU reads it, while the O
+// accumulator stays in AGPRs.  Because the compiler does not know these are
+// MFMAs, their consumers must leave the wait states the hardware requires
+// between an XDL result and a VALU read (the fixed-slot schedule below does).
+__device__ __forceinline__ void mfma_vgpr_first(f32x16& d, bf16x8 a, bf16x8 b) {
+  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(d) : "v"(a), "v"(b));
+}
+__device__ __forceinline__ void mfma_vgpr_acc(f32x16& d, bf16x8 a, bf16x8 b) {
+  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(d) : "v"(a), "v"(b));
+}
+
+// 16 wait states between the last of those MFMAs and any VALU read of their
+// results; the scheduling fences keep the compiler from moving work across.
+__device__ __forceinline__ void xdl_result_guard() {
+  __builtin_amdgcn_sched_barrier(0);
+  asm volatile("s_nop 7\n\ts_nop 7" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
+}
+
 // ------------------------------------------------------- bf16 path, DMA layout
 // K and V tiles go global -> LDS with 16-byte buffer loads that write LDS
 // directly (lane l of one load fills bytes [16 l, 16 l + 16) of a 1 KB block),
@@ -220,6 +242,22 @@ struct Bf16Dma {
         const int off = addr(32 * kb, 32 * kk) - addr(0, 0);
         bf16x8 a = *(const __attribute__((address_space(3))) bf16x8*)(kt + kbase + off);
         s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, f.v[kk], s[kb], 0, 0, 0);
+      }
+    }
+  }
+
+  // The same product with the accumulators in VGPRs (for kernels run at one wave per
+  // SIMD, whose MFMAs the compiler would otherwise give AGPR results).  The caller
+  // must leave the XDL-to-VALU wait states (xdl_result_guard) before reading s.
+  __device__ static void scores_vgpr(f32x16 (&s)[kBN / 32], const QFrag& f, const lds_char* kt, int kbase) {
+#pragma unroll
+    for (int kk = 0; kk < NQ; ++kk) {
+#pragma unroll
+      for (int kb = 0; kb < kBN / 32; ++kb) {
+        const int off = addr(32 * kb, 32 * kk) - addr(0, 0);
+        bf16x8 a = *(const __attribute__((address_space(3))) bf16x8*)(kt + kbase + off);
+        if (kk == 0) mfma_vgpr_first(s[kb], a, f.v[0]);
+        else mfma_vgpr_acc(s[kb], a, f.v[kk]);
       }
     }
   }
@@ -497,20 +535,6 @@ __device__ __forceinline__ void attn_fwd_body(const FwdArgs& a, char* smem) {
     P::accumulate(o, s, vs, lane);
   }
   write_rows<P, D, PARTIAL>(a, w, o, 1.0f / l, (m + __builtin_amdgcn_logf(l)) * kLn2, h_half);
-}
-
-// S^T accumulation with the accumulator in VGPRs.  With one wave per SIMD the
-// compiler gives every MFMA the AGPR form, which would make each score travel
-// AGPR -> VGPR (v_accvgpr_read) before the softmax can touch it; written out here
-// the score MFMAs keep their result where the VALU reads it, while the O
-// accumulator stays in AGPRs.  Because the compiler does not know these are
-// MFMAs, their consumers must leave the wait states the hardware requires
-// between an XDL result and a VALU read (the fixed-slot schedule below does).
-__device__ __forceinline__ void mfma_vgpr_first(f32x16& d, bf16x8 a, bf16x8 b) {
-  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(d) : "v"(a), "v"(b));
-}
-__device__ __forceinline__ void mfma_vgpr_acc(f32x16& d, bf16x8 a, bf16x8 b) {
-  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(d) : "v"(a), "v"(b));
 }
 
 // Workgroup barrier that orders LDS only: tile loads in flight (vmcnt) are not
