@@ -1,20 +1,26 @@
 """Build libattnprefix.so in-tree with hipcc for gfx950.
 
 Usage: ``python -m long_context_prefix_amd.build`` (or ``build_library()``).
+The device assembly of the same compile is kept in ``_build/`` and checked
+for early reads of inline MFMA results (``isa_check``); a finding fails the
+build.
 """
 
 from __future__ import annotations
 
+import glob
 import os
 import shutil
 import subprocess
 import sys
+import tempfile
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 SRC = os.path.join(PKG, "csrc", "attn_api.hip")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libattnprefix.so")
+ASM = os.path.join(PKG, "_build", "libattnprefix.gfx950.s")
 ARCH = "gfx950"
 
 
@@ -40,14 +46,27 @@ def compile_command(out: str) -> list:
 
 
 def build_library(verbose: bool = False) -> str:
+    from .isa_check import inline_mfma_hazards
+
     tmp = LIB + ".tmp"
-    cmd = compile_command(tmp)
+    cmd = compile_command(tmp) + ["-save-temps"]
     if verbose:
         print(" ".join(cmd), flush=True)
-    res = subprocess.run(cmd, capture_output=True, text=True)
-    if res.returncode != 0:
-        sys.stderr.write(res.stdout + res.stderr)
-        raise RuntimeError(f"hipcc failed with exit code {res.returncode}")
+    with tempfile.TemporaryDirectory() as work:  # -save-temps writes into the working directory
+        res = subprocess.run(cmd, capture_output=True, text=True, cwd=work)
+        if res.returncode != 0:
+            sys.stderr.write(res.stdout + res.stderr)
+            raise RuntimeError(f"hipcc failed with exit code {res.returncode}")
+        asm_files = glob.glob(os.path.join(work, f"*-hip-amdgcn-amd-amdhsa-{ARCH}.s"))
+        if len(asm_files) != 1:
+            raise RuntimeError(f"expected one device assembly file, found {asm_files}")
+        os.makedirs(os.path.dirname(ASM), exist_ok=True)
+        shutil.copyfile(asm_files[0], ASM)
+    with open(ASM) as f:
+        hazards = inline_mfma_hazards(f.read())
+    if hazards:
+        os.remove(tmp)
+        raise RuntimeError("inline MFMA result read too early:\n" + "\n".join(hazards[:10]))
     os.replace(tmp, LIB)
     return LIB
 

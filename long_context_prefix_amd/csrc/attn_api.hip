@@ -86,6 +86,7 @@ attn_status_t dispatch_fwd(const FwdArgs& a, int D, attn_dtype_t dtype, int64_t 
   return ATTN_ERR_UNSUPPORTED;
 }
 
+// WPE_DKDV = 0 selects the software-pipelined dk/dv kernel (one wave per SIMD).
 template <int D, int WPE_DQ, int WPE_DKDV>
 attn_status_t launch_bwd(const BwdArgs& base, int64_t rows, int64_t grid_dq, int64_t grid_dkdv, hipStream_t s) {
   (void)hipGetLastError();
@@ -99,7 +100,10 @@ attn_status_t launch_bwd(const BwdArgs& base, int64_t rows, int64_t grid_dq, int
   }
   if (grid_dkdv > 0) {
     a.n_tiles = (a.S + 127) / 128;
-    hipLaunchKernelGGL((bwd_dkdv_kernel<D, WPE_DKDV>), dim3((unsigned)grid_dkdv), dim3(kThreads), 0, s, a);
+    if constexpr (WPE_DKDV == 0)
+      hipLaunchKernelGGL((bwd_dkdv_pipe_kernel<D>), dim3((unsigned)grid_dkdv), dim3(kThreads), 0, s, a);
+    else
+      hipLaunchKernelGGL((bwd_dkdv_kernel<D, WPE_DKDV>), dim3((unsigned)grid_dkdv), dim3(kThreads), 0, s, a);
   }
   return hipGetLastError() == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
 }
@@ -169,7 +173,7 @@ attn_status_t attn_prefix_bwd(const void* q, const void* k, const void* v, const
     fprintf(stderr, "[attn_prefix] prefix_bwd D=%d B=%d H=%d Tq=%d S=%d grid dq=%lld dkdv=%lld\n", D, B, H, Tq, S,
             (long long)grid_dq, (long long)grid_dkdv);
   if (D == 64) return launch_bwd<64, 2, 2>(a, rows, grid_dq, grid_dkdv, st);
-  return launch_bwd<128, 2, 1>(a, rows, grid_dq, grid_dkdv, st);
+  return launch_bwd<128, 2, 0>(a, rows, grid_dq, grid_dkdv, st);
 }
 
 int attn_splitkv_num_chunks(int S, int chunk) {

@@ -317,4 +317,203 @@ void bwd_dkdv_kernel(BwdArgs a) {
   }
 }
 
+// ---------------------------------------------------- dk, dv (pipelined)
+// The same computation at one wave per SIMD with the loop software-pipelined:
+// iteration t issues S_{t+1} = Q_{t+1} K^T and dP_{t+1} = dO_{t+1} V^T on the
+// MFMA pipe while the VALU turns S_t, dP_t into P_t and dS_t, then accumulates
+// dV += dO_t^T P_t and dK += Q_t^T dS_t.  Q and dO tiles are triple-buffered
+// (t and t+1 are read while t+2 loads), the per-query statistics too.  The
+// iteration is written as fixed slots (one MFMA, the operand read a few slots
+// ahead, a share of the softmax work and of the next tiles' DMA) separated by
+// scheduling fences, as in the D = 256 forward.  The loop always runs an even
+// number of identical iterations: a query tile past Tq is zero-filled by its
+// (empty) load and its statistics give P = 0, so the spare iteration adds
+// nothing, and no straight-line copy of the pipelined body (where the register
+// allocator could move a fresh MFMA result with a VALU copy) is ever needed.
+template <int D>
+__global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads), amdgpu_waves_per_eu(1, 1)))
+void bwd_dkdv_pipe_kernel(BwdArgs a) {
+  using P = Bf16Dma<D>;
+  constexpr int kKeysPerWg = 128;
+  constexpr int R = 2;                         // operand reads issued this many slots ahead
+  constexpr int NS = P::NQ * (kBN / 32);       // MFMAs of S (and of dP) per tile
+  constexpr int NA = 2 * NS;                   // phase A slots: S and dP interleaved
+  constexpr int NV = (D / 32) * (kBN / 16);    // MFMAs of dV (and of dK) per tile
+  constexpr int NB = 2 * NV;                   // phase B slots
+  constexpr int NE = kBN / 2;                  // softmax elements per lane per tile
+  constexpr int EPS = (NE + NA - 1) / NA;      // softmax elements per phase A slot
+  static_assert(NA * EPS >= NE, "softmax elements must fit the slots");
+  __shared__ __attribute__((aligned(16))) char smem_raw[6 * P::TILE_BYTES];
+  __shared__ __attribute__((aligned(16))) float stat[3][2][kBN];  // [buffer][lse*log2e | delta][query]
+  lds_char* const smem = (lds_char*)smem_raw;
+  auto qb_ = [&](int i) { return smem + i * P::TILE_BYTES; };        // Q buffers 0..2
+  auto gb_ = [&](int i) { return smem + (3 + i) * P::TILE_BYTES; };  // dO buffers 0..2
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+  const int h_half = lane >> 5;
+  int wg = blockIdx.x;
+  const int kblk = wg % a.n_tiles;
+  wg /= a.n_tiles;
+  const int h = wg % a.H, b = wg / a.H;
+  int n = a.kv_len[b];
+  n = n < 0 ? 0 : (n > a.S ? a.S : n);
+  const int64_t bh = (int64_t)b * a.H + h;
+  const int key = kblk * kKeysPerWg + wave * 32 + (lane & 31);
+  const bool key_in = key < a.S;
+  const bool key_ok = key < n;
+  const int64_t krow = bh * a.S + key;
+  if (kblk * kKeysPerWg >= n || a.Tq == 0) {
+    if (key_in) {
+      store_zero_rows_bf16<D>(a.dk, krow, h_half);
+      store_zero_rows_bf16<D>(a.dv, krow, h_half);
+    }
+    return;
+  }
+  const int TQ = (a.Tq + kBN - 1) / kBN;
+  auto nq_of = [&](int t) {
+    const int r = a.Tq - t * kBN;
+    return r < 0 ? 0 : (r > kBN ? kBN : r);
+  };
+  const uint16_t* qg = reinterpret_cast<const uint16_t*>(a.q) + bh * a.Tq * D;
+  const uint16_t* gg = reinterpret_cast<const uint16_t*>(a.dout) + bh * a.Tq * D;
+  auto q_tile = [&](int t) { return make_rsrc(qg + (int64_t)t * kBN * D, (uint32_t)nq_of(t) * (D * 2)); };
+  auto g_tile = [&](int t) { return make_rsrc(gg + (int64_t)t * kBN * D, (uint32_t)nq_of(t) * (D * 2)); };
+  const float* lse_bh = a.lse + bh * a.Tq;
+  const float* del_bh = a.delta + bh * a.Tq;
+  auto stat_load = [&](int t) -> float {
+    const int qi = t * kBN + (tid & 63);
+    if (tid < 64) return qi < a.Tq ? lse_bh[qi] * kLog2e : __builtin_inff();
+    if (tid < 128) return qi < a.Tq ? del_bh[qi] : 0.0f;
+    return 0.0f;
+  };
+
+  typename P::QFrag kf, vf;
+  const int64_t src = bh * a.S + (key_ok ? key : 0);
+  P::load_q(kf, reinterpret_cast<const uint16_t*>(a.k) + src * D, key_ok, h_half);
+  P::load_q(vf, reinterpret_cast<const uint16_t*>(a.v) + src * D, key_ok, h_half);
+  const float c = a.scale_log2;
+  const int kbase = P::k_base(lane);
+  const int vbase = P::v_base(lane);
+
+  f32x16 dk[D / 32], dv[D / 32];
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db) {
+    dk[db] = f32x16{};
+    dv[db] = f32x16{};
+  }
+
+  // prologue: tiles 0 and 1 (and their statistics) in LDS, S_0 and dP_0 in registers
+  P::dma_tile(q_tile(0), qb_(0), wave_u, lane);
+  P::dma_tile(g_tile(0), gb_(0), wave_u, lane);
+  P::dma_tile(q_tile(1), qb_(1), wave_u, lane);  // empty past Tq: zero fill
+  P::dma_tile(g_tile(1), gb_(1), wave_u, lane);
+  {
+    const float x0 = stat_load(0);
+    const float x1 = stat_load(1);
+    if (tid < 128) {
+      stat[0][tid >> 6][tid & 63] = x0;
+      stat[1][tid >> 6][tid & 63] = x1;
+    }
+  }
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+  __syncthreads();
+  f32x16 s0[kBN / 32], d0[kBN / 32], s1[kBN / 32], d1[kBN / 32];
+  P::scores_vgpr(s0, kf, qb_(0), kbase);
+  P::scores_vgpr(d0, vf, gb_(0), kbase);
+  xdl_result_guard();
+
+  auto iteration = [&](int t, f32x16 (&sc)[kBN / 32], f32x16 (&dc)[kBN / 32], f32x16 (&sn)[kBN / 32],
+                       f32x16 (&dn)[kBN / 32]) {
+    const int bc = t % 3, bn = (t + 1) % 3, bf = (t + 2) % 3;
+    const __amdgpu_buffer_rsrc_t q_rs = q_tile(t + 2), g_rs = g_tile(t + 2);
+    const float next_stat = stat_load(t + 2);
+    // this tile's per-query statistics, four queries at a time: softmax element e is register
+    // e % 16 of block e / 16, query 32 (e / 16) + 8 ((e % 16) / 4) + 4 h + e % 4
+    auto stat4 = [&](int g, int which) {
+      const int q0 = 32 * (g >> 2) + 8 * (g & 3) + 4 * h_half;
+      return *reinterpret_cast<const f32x4*>(&stat[bc][which][q0]);
+    };
+    f32x4 Lq[2], Dq[2];  // groups g and g + 1 (ring of two)
+    Lq[0] = stat4(0, 0);
+    Dq[0] = stat4(0, 1);
+    u32x4 ppk[kBN / 16], dpk[kBN / 16];
+    float pe[NE], de[NE];
+    bf16x8 fr[R];
+#pragma unroll
+    for (int i = 0; i < R; ++i) fr[i] = P::k_frag((i & 1) ? gb_(bn) : qb_(bn), kbase, i >> 1);
+    bf16x8 tr[R];
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int i = 0; i < NA; ++i) {
+      {
+        const int j = i >> 1, kb = j & 1, kk = j >> 1;
+        f32x16& acc = (i & 1) ? dn[kb] : sn[kb];
+        if (kk == 0) mfma_vgpr_first(acc, fr[i % R], (i & 1) ? vf.v[0] : kf.v[0]);
+        else mfma_vgpr_acc(acc, fr[i % R], (i & 1) ? vf.v[kk] : kf.v[kk]);
+        if (i + R < NA) {
+          const int ii = i + R;
+          fr[i % R] = P::k_frag((ii & 1) ? gb_(bn) : qb_(bn), kbase, ii >> 1);
+        }
+      }
+      if (i >= NA - R) {  // operands of the first phase B slots
+        const int ii = i - (NA - R);
+        tr[ii] = P::v_frag((ii & 1) ? qb_(bc) : gb_(bc), vbase, ii >> 1);
+      }
+      // the next tiles' DMA (past the last tile the resource is empty and the loads
+      // zero-fill the buffer)
+      if (i < P::DMA_PER_WAVE) P::dma_block(q_rs, qb_(bf), wave_u, lane, i);
+      else if (i < 2 * P::DMA_PER_WAVE) P::dma_block(g_rs, gb_(bf), wave_u, lane, i - P::DMA_PER_WAVE);
+#pragma unroll
+      for (int u = 0; u < EPS; ++u) {
+        const int e = i * EPS + u;
+        if (e < NE) {
+          const int kb = e >> 4, r = e & 15, g = e >> 2;
+          if ((e & 3) == 0 && g + 1 < NE / 4) {  // fetch the next group's statistics
+            Lq[(g + 1) & 1] = stat4(g + 1, 0);
+            Dq[(g + 1) & 1] = stat4(g + 1, 1);
+          }
+          const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[kb][r], c, -Lq[g & 1][e & 3]));
+          pe[e] = p;
+          de[e] = p * (dc[kb][r] - Dq[g & 1][e & 3]);
+          if (e & 1) {
+            ppk[e >> 3][(e & 7) >> 1] = pack_bf16x2(pe[e - 1], p);
+            dpk[e >> 3][(e & 7) >> 1] = pack_bf16x2(de[e - 1], de[e]);
+          }
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+#pragma unroll
+    for (int i = 0; i < NB; ++i) {
+      const int j = i >> 1, ks = j / (D / 32), db = j % (D / 32);
+      if (i & 1) dk[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr[i % R], __builtin_bit_cast(bf16x8, dpk[ks]), dk[db], 0, 0, 0);
+      else dv[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr[i % R], __builtin_bit_cast(bf16x8, ppk[ks]), dv[db], 0, 0, 0);
+      if (i + R < NB) {
+        const int ii = i + R;
+        tr[i % R] = P::v_frag((ii & 1) ? qb_(bc) : gb_(bc), vbase, ii >> 1);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    if (tid < 128) stat[bf][tid >> 6][tid & 63] = next_stat;
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // this wave's tile loads have landed
+    lds_barrier();
+  };
+
+  for (int t = 0; t < TQ; t += 2) {  // an odd TQ ends with one empty tile
+    iteration(t, s0, d0, s1, d1);
+    iteration(t + 1, s1, d1, s0, d0);
+  }
+  if (key_in) {
+    if (key_ok) {
+      store_rows_bf16<D>(a.dk, krow, dk, a.scale, h_half);
+      store_rows_bf16<D>(a.dv, krow, dv, 1.0f, h_half);
+    } else {
+      store_zero_rows_bf16<D>(a.dk, krow, h_half);
+      store_zero_rows_bf16<D>(a.dv, krow, h_half);
+    }
+  }
+}
+
 }  // namespace lcp
