@@ -23,10 +23,12 @@ def test_early_store_is_found():
 
 
 def test_guarded_read_is_clean():
-    asm = _asm("s_nop 7", "s_nop 7", "v_add_f32 v1, v2, v3", "v_add_f32 v1, v2, v3", "v_add_f32 v1, v2, v3",
-               "v_add_f32 v1, v2, v3", "v_add_f32 v1, v2, v3", "v_add_f32 v1, v2, v3", "v_add_f32 v1, v2, v3",
-               "v_mov_b32 v40, v12")
+    # 16 wait states of s_nop plus 8 instructions: the read comes after 24 wait states
+    asm = _asm("s_nop 7", "s_nop 7", *(["v_add_f32 v1, v2, v3"] * 8), "v_mov_b32 v40, v12")
     assert inline_mfma_hazards(asm) == []
+    # one instruction fewer is one wait state short
+    asm = _asm("s_nop 7", "s_nop 7", *(["v_add_f32 v1, v2, v3"] * 7), "v_mov_b32 v40, v12")
+    assert len(inline_mfma_hazards(asm)) == 1
 
 
 def test_accumulation_chain_and_unrelated_reads_are_clean():
