@@ -106,6 +106,7 @@ def main() -> int:
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--no-splitkv", action="store_true", help="skip the split-KV workload")
+    ap.add_argument("--no-backward", action="store_true", help="skip the backward workload")
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle timing and parity sample")
     ap.add_argument("--cpu-rows", type=int, default=4096, help="oracle query rows per head for the CPU baseline")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -282,6 +283,58 @@ def main() -> int:
             },
         }
         del q, k, v, po, pl, out, lse
+        torch.cuda.empty_cache()
+
+    # ------------------------------------------------------------- backward
+    if not args.no_backward:
+        wb = WORKLOADS["ragged_32k"]
+        log(f"generating {wb.name}: B={wb.B} H={wb.H} D={wb.D} Tq={wb.Tq} S={wb.S} kv_len={wb.lens().tolist()}")
+        q, k, v, kv = make_workload(wb, device="cuda")
+        blens = wb.lens()
+        pairs = float(wb.H) * wb.Tq * float(blens.sum())
+        out = torch.empty_like(q)
+        lse = torch.empty((wb.B, wb.H, wb.Tq), dtype=torch.float32, device="cuda")
+        g = torch.Generator(device="cpu").manual_seed(wb.seed + 77)
+        dout = torch.randn(q.shape, generator=g, dtype=torch.float32).to(torch.bfloat16).to("cuda")
+        dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+        delta = torch.empty_like(lse)
+
+        def fwd_b():
+            _lib.attn_prefix_fwd(q, k, v, kv, wb.scale, out=out, lse=lse)
+
+        def bwd_b():
+            _lib.attn_prefix_bwd(q, k, v, kv, out, dout, lse, wb.scale, dq=dq, dk=dk, dv=dv, delta=delta)
+
+        for _ in range(args.warmup):
+            fwd_b()
+            bwd_b()
+        torch.cuda.synchronize()
+        steps = max(1, args.steps)
+        log(f"timing {steps} forward + backward steps")
+        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+        for e0, e1, e2 in evs:
+            e0.record()
+            fwd_b()
+            e1.record()
+            bwd_b()
+            e2.record()
+        torch.cuda.synchronize()
+        t_f = sum(a.elapsed_time(b) for a, b, _ in evs) / steps
+        t_b = sum(b.elapsed_time(c) for _, b, c in evs) / steps
+        alg_b = 10.0 * wb.D * pairs  # dV, dP, dQ, dK and the recomputed S: five products of 2 D per pair
+        log(f"backward: fwd {t_f:.3f} ms, bwd {t_b:.3f} ms, {alg_b / (t_b * 1e-3) / 1e12:.1f} TFLOP/s")
+        result["backward"] = {
+            "workload": wb.name, "B": wb.B, "H": wb.H, "head_dim": wb.D, "T_q": wb.Tq, "S": wb.S,
+            "kv_len": [int(x) for x in blens],
+            "forward_ms": round(t_f, 4), "backward_ms": round(t_b, 4),
+            "forward_tflops": round(4.0 * wb.D * pairs / (t_f * 1e-3) / 1e12, 2),
+            "value": round(alg_b / (t_b * 1e-3) / 1e12, 2),
+            "unit": "TFLOP/s (algorithmic: 10 D per (query, valid key) pair and head)",
+            "pct_mfma_peak": round(100 * alg_b / (t_b * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 2),
+            "executed_tflops": round(14.0 * wb.D * pairs / (t_b * 1e-3) / 1e12, 2),
+            "kernels": "bwd_delta_kernel, bwd_dq_kernel (S, dP, dQ), bwd_dkdv_pipe_kernel (S, dP, dV, dK)",
+        }
+        del q, k, v, out, lse, dout, dq, dk, dv, delta
         torch.cuda.empty_cache()
 
     if args.copy_calibration:
