@@ -74,3 +74,25 @@ def gather_rows(x: torch.Tensor, rows: np.ndarray) -> torch.Tensor:
 
 def default_scale(d: int) -> float:
     return 1.0 / math.sqrt(d)
+
+
+# Backward (bf16 inputs): rel-L2 per gradient tensor, and max-abs relative to the
+# largest reference magnitude; the derivation is in tests/test_gpu_bwd.py.
+GRAD_REL_L2 = 5e-3
+GRAD_MAX_ABS_REL = 2e-2
+
+
+def assert_grad_parity(name: str, got, ref, what: str = ""):
+    g = to64(got) if isinstance(got, torch.Tensor) else np.asarray(got, np.float64)
+    r = np.asarray(ref, np.float64)
+    assert g.shape == r.shape, (g.shape, r.shape)
+    assert np.isfinite(g).all(), f"{what} {name}: non-finite"
+    rn = float(np.linalg.norm(r))
+    err = float(np.linalg.norm(g - r))
+    rel = err / rn if rn > 0 else err
+    mx = float(np.abs(g - r).max()) if g.size else 0.0
+    top = float(np.abs(r).max()) if r.size else 0.0
+    log(f"{what} {name}: rel_l2={rel:.3e} max_abs={mx:.3e} (ref max {top:.3e})")
+    assert rel <= GRAD_REL_L2, f"{what} {name}: rel_l2 {rel:.3e}"
+    assert mx <= GRAD_MAX_ABS_REL * max(top, 1e-6), f"{what} {name}: max_abs {mx:.3e}"
+    return rel, mx

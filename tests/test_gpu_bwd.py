@@ -22,13 +22,11 @@ import torch
 from long_context_prefix_amd import _lib, prefix_attention
 from long_context_prefix_amd.workloads import make_inputs
 from oracle import ref_prefix_bwd
-from tests.parity import log, to64
+from tests.parity import assert_grad_parity, log, to64
 
 pytestmark = pytest.mark.gpu
 
 DEV = "cuda"
-REL_L2 = 5e-3
-MAX_ABS_REL = 2e-2
 
 
 def _grads(q, k, v, kv, scale, seed):
@@ -41,17 +39,7 @@ def _grads(q, k, v, kv, scale, seed):
 
 
 def _check(name, got, ref, what):
-    g = to64(got)
-    r = np.asarray(ref, np.float64)
-    assert np.isfinite(g).all(), f"{what} {name}: non-finite"
-    rn = float(np.linalg.norm(r))
-    err = float(np.linalg.norm(g - r))
-    rel = err / rn if rn > 0 else err
-    mx = float(np.abs(g - r).max()) if g.size else 0.0
-    top = float(np.abs(r).max()) if r.size else 0.0
-    log(f"{what} {name}: rel_l2={rel:.3e} max_abs={mx:.3e} (ref max {top:.3e})")
-    assert rel <= REL_L2, f"{what} {name}: rel_l2 {rel:.3e}"
-    assert mx <= MAX_ABS_REL * max(top, 1e-6), f"{what} {name}: max_abs {mx:.3e}"
+    assert_grad_parity(name, got, ref, what)
 
 
 def _compare(q, k, v, kv, scale, seed, what):

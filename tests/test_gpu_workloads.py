@@ -11,8 +11,8 @@ import torch
 
 from long_context_prefix_amd import _lib
 from long_context_prefix_amd.workloads import WORKLOADS, make_workload, sample_rows
-from oracle import ref_prefix_fwd, ref_splitkv_partial
-from tests.parity import assert_parity, gather_rows, log, to64
+from oracle import ref_prefix_bwd, ref_prefix_fwd, ref_splitkv_partial
+from tests.parity import assert_grad_parity, assert_parity, gather_rows, log, to64
 
 pytestmark = [pytest.mark.gpu, pytest.mark.slow]
 
@@ -59,3 +59,33 @@ def test_inducing_splitkv_workload():
             rpo, rpl = ref_splitkv_partial(qb, to64(k[b:b + 1]), to64(v[b:b + 1]), [n], w.scale, w.chunk)
             assert_parity(po[b:b + 1, :, 24], pl[b:b + 1, :, 24], rpo[:, :, 24], rpl[:, :, 24], "bf16",
                           f"partial chunk 24 seq {b}")
+
+
+@pytest.mark.timeout(900)
+def test_backward_ragged_32k():
+    """The backward at its full size: dq on seeded query rows of every (b, h); dk and dv
+    over every key of one head of the n = 6153 element (all 32768 queries feed them);
+    zero gradients on every padded slot."""
+    w = WORKLOADS["ragged_32k"]
+    lens = w.lens()
+    log(f"backward workload {w.name}: kv_len={lens.tolist()}")
+    q, k, v, kv = make_workload(w, device=DEV)
+    out, lse = _lib.attn_prefix_fwd(q, k, v, kv, w.scale)
+    g = torch.Generator(device="cpu").manual_seed(w.seed + 77)
+    dout = torch.randn(q.shape, generator=g, dtype=torch.float32).to(torch.bfloat16).to(DEV)
+    dq, dk, dv = _lib.attn_prefix_bwd(q, k, v, kv, out, dout, lse, w.scale)
+    torch.cuda.synchronize()
+    for b, n in enumerate(lens):
+        assert torch.all(dk[b, :, n:] == 0) and torch.all(dv[b, :, n:] == 0), f"padded gradient, element {b}"
+    sel = sample_rows(w.seed + 1, w.Tq, 32, w.B * w.H)
+    nmax = int(lens.max())
+    rq, _, _ = ref_prefix_bwd(to64(gather_rows(q, sel)), to64(k[:, :, :nmax]), to64(v[:, :, :nmax]), lens, w.scale,
+                              to64(gather_rows(dout, sel)))
+    assert_grad_parity("dq (sampled rows)", gather_rows(dq, sel), rq, w.name)
+    b, h = 1, 0
+    n = int(lens[b])
+    sl = (slice(b, b + 1), slice(h, h + 1))
+    _, rk, rv = ref_prefix_bwd(to64(q[sl]), to64(k[sl][:, :, :n]), to64(v[sl][:, :, :n]), [n], w.scale,
+                               to64(dout[sl]))
+    assert_grad_parity("dk (one head)", dk[sl][:, :, :n], rk, w.name)
+    assert_grad_parity("dv (one head)", dv[sl][:, :, :n], rv, w.name)
