@@ -729,7 +729,7 @@ __device__ __forceinline__ void bf16_fwd_dma(const FwdArgs& a, char* smem_generi
       for (int i = 0; i < R; ++i) kf[i] = P::k_frag(k_next, kbase, i);
       const float nm = -sm.m;
       float acc[4] = {0.f, 0.f, 0.f, 0.f};
-      float pe[kBN / 2];
+      float pe[kBN / 2], xe[kBN / 2];
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int i = 0; i < NS; ++i) {
@@ -746,11 +746,19 @@ __device__ __forceinline__ void bf16_fwd_dma(const FwdArgs& a, char* smem_generi
         }
 #pragma unroll
         for (int t = 0; t < EPS; ++t) {
-          const int e = i * EPS + t;  // register e % 16 of S^T block e / 16
-          const float x = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[e >> 4][e & 15], c, nm));
-          pe[e] = x;
-          acc[e & 3] += x;
-          if (e & 1) pk[e >> 3][(e & 7) >> 1] = pack_bf16x2(pe[e - 1], x);
+          // element e (register e % 16 of S^T block e / 16) is staged over three steps so
+          // that no instruction waits on the one just before it: the fma of element e + 2,
+          // the exp2 of element e + 1, then the sum and bf16 pack of element e
+          const int e = i * EPS + t;
+          if (e == 0) {
+            xe[0] = __builtin_fmaf(sc[0][0], c, nm);
+            xe[1] = __builtin_fmaf(sc[0][1], c, nm);
+            pe[0] = __builtin_amdgcn_exp2f(xe[0]);
+          }
+          if (e + 2 < kBN / 2) xe[e + 2] = __builtin_fmaf(sc[(e + 2) >> 4][(e + 2) & 15], c, nm);
+          if (e + 1 < kBN / 2) pe[e + 1] = __builtin_amdgcn_exp2f(xe[e + 1]);
+          acc[e & 3] += pe[e];
+          if (e & 1) pk[e >> 3][(e & 7) >> 1] = pack_bf16x2(pe[e - 1], pe[e]);
         }
         __builtin_amdgcn_sched_barrier(0);
       }
