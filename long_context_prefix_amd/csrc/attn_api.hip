@@ -59,11 +59,20 @@ attn_status_t check_fwd(const void* q, const void* k, const void* v, const int32
 
 template <class P, int D, bool PARTIAL, int W>
 attn_status_t launch_fwd(const FwdArgs& a, int64_t grid, hipStream_t stream, const char* tag) {
+  // one query tile per head: every K/V tile is read by one workgroup, so stream it
+  const bool stream_kv = !P::kIsF32 && a.n_qtiles == 1;
   if (verbose())
-    fprintf(stderr, "[attn_prefix] %s D=%d %s grid=%lld block=%d lds=%d waves_per_eu=%d\n", tag, D,
-            P::kIsF32 ? "f32" : "bf16", (long long)grid, kThreads, P::LDS_BYTES, W);
+    fprintf(stderr, "[attn_prefix] %s D=%d %s grid=%lld block=%d lds=%d waves_per_eu=%d%s\n", tag, D,
+            P::kIsF32 ? "f32" : "bf16", (long long)grid, kThreads, P::LDS_BYTES, W, stream_kv ? " streaming" : "");
   (void)hipGetLastError();  // clear an error left by unrelated earlier calls
-  hipLaunchKernelGGL((attn_fwd_kernel<P, D, PARTIAL, W>), dim3((unsigned)grid), dim3(kThreads), 0, stream, a);
+  if constexpr (!P::kIsF32) {
+    if (stream_kv) {
+      hipLaunchKernelGGL((attn_fwd_kernel<P, D, PARTIAL, W, true>), dim3((unsigned)grid), dim3(kThreads), 0, stream,
+                         a);
+      return hipGetLastError() == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
+    }
+  }
+  hipLaunchKernelGGL((attn_fwd_kernel<P, D, PARTIAL, W, false>), dim3((unsigned)grid), dim3(kThreads), 0, stream, a);
   return hipGetLastError() == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
 }
 
