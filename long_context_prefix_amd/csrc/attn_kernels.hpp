@@ -23,6 +23,10 @@
 // write LDS directly (no staging registers), K operands are 16-byte LDS reads
 // and V^T operands come from the transposing LDS read; fp32 inputs use a
 // plain register-staged tile loop with fp32 MFMA.
+//
+// The file also holds the log-sum-exp merge of split-KV partials and the
+// device-side prefix-mask detector; the backward kernels, built on the same
+// tile layout, are in attn_bwd_kernels.hpp.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -75,9 +79,6 @@ __device__ __forceinline__ float pair_sum(float x) {
 // Key index (within a tile) held by S^T register r of a lane in half h.
 __device__ __forceinline__ int st_key(int kb, int r, int h) { return 32 * kb + 8 * (r >> 2) + 4 * h + (r & 3); }
 
-// Position of key j of a tile in the permuted V^T layout (an involution).
-__host__ __device__ constexpr int vt_pos(int j) { return (j & ~12) | ((j & 4) << 1) | ((j & 8) >> 1); }
-
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   // round to nearest even (v_cvt_pk_bf16_f32)
   typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
@@ -95,10 +96,6 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, ui
   const uint32_t n = __builtin_amdgcn_readfirstlane(bytes);
   void* b = reinterpret_cast<void*>(((uint64_t)hi << 32) | lo);
   return __builtin_amdgcn_make_buffer_rsrc(b, (short)0, (int)n, 0x00020000);
-}
-
-__device__ __forceinline__ u32x4 buf_load16(__amdgpu_buffer_rsrc_t rs, uint32_t off) {
-  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, (int)off, 0, 0));
 }
 
 // S^T accumulation with the accumulator in VGPRs.  With one wave per SIMD the
