@@ -150,8 +150,8 @@ attn_status_t attn_prefix_mask_to_kv_len(const uint8_t* mask, int B, int S, int6
  *   dq         : device bf16 [B,H,Tq,D]; dk, dv: device bf16 [B,H,S,D]; every
  *                element is written (dk = dv = 0 on slots j >= n_b; dq = 0 for
  *                batch elements with n_b = 0)
- * Supported: dtype ATTN_BF16 with D in {64, 128} (other dtypes or head dims
- * return ATTN_ERR_UNSUPPORTED).  Three kernels are enqueued on `stream`
+ * Supported: dtype ATTN_BF16 with D in {64, 128, 256} (fp32 inputs return
+ * ATTN_ERR_UNSUPPORTED).  Three kernels are enqueued on `stream`
  * (delta, dq, dk/dv); no atomics, so results are deterministic.  Tq = 0 zeroes
  * dk and dv; S = 0 zeroes dq. */
 attn_status_t attn_prefix_bwd(const void* q, const void* k, const void* v, const int32_t* kv_len, const void* out,

@@ -248,7 +248,7 @@ def sdpa_prefix(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, attn_mask: to
 def attn_prefix_bwd(q, k, v, kv_len, out, dout, lse, scale: Optional[float] = None,
                     dq: Optional[torch.Tensor] = None, dk: Optional[torch.Tensor] = None,
                     dv: Optional[torch.Tensor] = None, delta: Optional[torch.Tensor] = None):
-    """Gradients (dq, dk, dv) of the prefix-masked forward, bf16, D in {64, 128}.
+    """Gradients (dq, dk, dv) of the prefix-masked forward, bf16, D in {64, 128, 256}.
 
     ``out`` and ``lse`` are the forward's results; ``delta`` is an optional fp32
     [B, H, Tq] workspace (rowsum(dout * out)).  dk and dv are zero on padded slots.

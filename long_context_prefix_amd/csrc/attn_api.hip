@@ -141,7 +141,7 @@ attn_status_t attn_prefix_bwd(const void* q, const void* k, const void* v, const
                               attn_dtype_t dtype, float* delta, void* dq, void* dk, void* dv, void* stream) {
   if (dtype != ATTN_BF16 && dtype != ATTN_F32) return ATTN_ERR_DTYPE;
   if (B < 0 || H < 0 || Tq < 0 || S < 0 || D < 0) return ATTN_ERR_SHAPE;
-  if (dtype != ATTN_BF16 || (D != 64 && D != 128)) return ATTN_ERR_UNSUPPORTED;
+  if (dtype != ATTN_BF16 || (D != 64 && D != 128 && D != 256)) return ATTN_ERR_UNSUPPORTED;
   if (!isfinite(scale)) return ATTN_ERR_ARG;
   if (B == 0 || H == 0 || (Tq == 0 && S == 0)) return ATTN_OK;
   if (!kv_len) return ATTN_ERR_NULLPTR;
@@ -182,7 +182,8 @@ attn_status_t attn_prefix_bwd(const void* q, const void* k, const void* v, const
     fprintf(stderr, "[attn_prefix] prefix_bwd D=%d B=%d H=%d Tq=%d S=%d grid dq=%lld dkdv=%lld\n", D, B, H, Tq, S,
             (long long)grid_dq, (long long)grid_dkdv);
   if (D == 64) return launch_bwd<64, 2, 2>(a, rows, grid_dq, grid_dkdv, st);
-  return launch_bwd<128, 2, 0>(a, rows, grid_dq, grid_dkdv, st);
+  if (D == 128) return launch_bwd<128, 2, 0>(a, rows, grid_dq, grid_dkdv, st);
+  return launch_bwd<256, 1, 1>(a, rows, grid_dq, grid_dkdv, st);
 }
 
 int attn_splitkv_num_chunks(int S, int chunk) {
@@ -197,7 +198,7 @@ const char* attn_status_string(attn_status_t s) {
     case ATTN_ERR_SHAPE: return "a size is negative or exceeds the library limits";
     case ATTN_ERR_DTYPE: return "unknown dtype (expected ATTN_BF16 or ATTN_F32)";
     case ATTN_ERR_UNSUPPORTED:
-      return "unsupported head dim or dtype for this call (forward: D 64/128/256; backward: bf16, D 64/128)";
+      return "unsupported head dim or dtype for this call (D 64/128/256; the backward takes bf16 only)";
     case ATTN_ERR_ALIGN: return "a tensor pointer is misaligned (16 bytes required; 4 for kv_len and lse)";
     case ATTN_ERR_CHUNK: return "chunk must be a positive multiple of 64";
     case ATTN_ERR_HIP: return "the HIP runtime reported an error";

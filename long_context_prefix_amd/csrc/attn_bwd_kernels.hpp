@@ -159,8 +159,9 @@ void bwd_dq_kernel(BwdArgs a) {
       P::dma_tile(v_tile(t + 1), vb_(cur ^ 1), wave_u, lane);
     }
     f32x16 s[kBN / 32], dp[kBN / 32];
-    P::scores(s, qf, kb_(cur), kbase);   // S^T = K Q^T
-    P::scores(dp, gf, vb_(cur), kbase);  // dP^T = V dO^T
+    P::scores_vgpr(s, qf, kb_(cur), kbase);   // S^T = K Q^T
+    P::scores_vgpr(dp, gf, vb_(cur), kbase);  // dP^T = V dO^T
+    xdl_result_guard();
     const int nv = nv_of(t);
     u32x4 pk[kBN / 16];
 #pragma unroll

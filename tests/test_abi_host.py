@@ -195,7 +195,7 @@ def test_bwd_argument_errors(L):
     assert call(dt=9) == DTYPE
     assert call(B=-1) == SHAPE
     assert call(dt=F32) == UNSUP  # the backward is bf16 only
-    assert call(D=256) == UNSUP
+    assert call(D=512) == UNSUP
     assert call(D=32) == UNSUP
     assert call(scale=float("nan")) == ARG
     for name in ("q", "kv", "out", "dout", "lse", "delta", "dq", "dk", "dv", "k", "v"):

@@ -56,7 +56,7 @@ def _compare(q, k, v, kv, scale, seed, what):
     return dq, dk, dv
 
 
-@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("D", [64, 128, 256])
 @pytest.mark.parametrize("Tq", [1, 17, 64, 150])
 def test_bwd_edge_matrix(D, Tq):
     S = 300
@@ -66,7 +66,7 @@ def test_bwd_edge_matrix(D, Tq):
     _compare(q, k, v, kv, 1.0 / math.sqrt(D), 77 + Tq, f"bwd D={D} Tq={Tq}")
 
 
-@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("D", [64, 128, 256])
 def test_bwd_multi_tile_sharp(D):
     """Several query and key tiles in both kernels, ragged tails, peaky attention (q x 3)."""
     B, H, Tq, S = 2, 3, 333, 777
@@ -114,10 +114,11 @@ def test_bwd_empty_sizes():
 
 
 def test_bwd_unsupported_is_an_error():
-    q, k, v, kv = make_inputs(1, 1, 8, 8, 256, [8], "bf16", 1.0, seed=972, device=DEV)
-    out, lse = _lib.attn_prefix_fwd(q, k, v, kv, 0.0625)
+    """The backward takes bf16 only: fp32 inputs are refused, not rerouted."""
+    q, k, v, kv = make_inputs(1, 1, 8, 8, 64, [8], "f32", 1.0, seed=972, device=DEV)
+    out, lse = _lib.attn_prefix_fwd(q, k, v, kv, 0.125)
     with pytest.raises(_lib.AttnError):
-        _lib.attn_prefix_bwd(q, k, v, kv, out, out, lse, 0.0625)
+        _lib.attn_prefix_bwd(q, k, v, kv, out, out, lse, 0.125)
 
 
 def test_autograd_wrapper_matches_oracle():
