@@ -332,7 +332,7 @@ def main() -> int:
             "unit": "TFLOP/s (algorithmic: 10 D per (query, valid key) pair and head)",
             "pct_mfma_peak": round(100 * alg_b / (t_b * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 2),
             "executed_tflops": round(14.0 * wb.D * pairs / (t_b * 1e-3) / 1e12, 2),
-            "kernels": "bwd_delta_kernel, bwd_dq_kernel (S, dP, dQ), bwd_dkdv_pipe_kernel (S, dP, dV, dK)",
+            "kernels": "bwd_delta_kernel, bwd_dq_slot_kernel (S, dP, dQ), bwd_dkdv_pipe_kernel (S, dP, dV, dK)",
         }
         del q, k, v, out, lse, dout, dq, dk, dv, delta
         torch.cuda.empty_cache()

@@ -105,7 +105,7 @@ attn_status_t launch_bwd(const BwdArgs& base, int64_t rows, int64_t grid_dq, int
     const int64_t g = (rows + rows_per_wg - 1) / rows_per_wg;
     hipLaunchKernelGGL((bwd_delta_kernel<D>), dim3((unsigned)g), dim3(256), 0, s, a, rows);
     a.n_tiles = (a.Tq + kBM - 1) / kBM;
-    hipLaunchKernelGGL((bwd_dq_kernel<D, WPE_DQ>), dim3((unsigned)grid_dq), dim3(kThreads), 0, s, a);
+    hipLaunchKernelGGL((bwd_dq_slot_kernel<D, WPE_DQ>), dim3((unsigned)grid_dq), dim3(kThreads), 0, s, a);
   }
   if (grid_dkdv > 0) {
     a.n_tiles = (a.S + 127) / 128;

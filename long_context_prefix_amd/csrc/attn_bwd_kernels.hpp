@@ -7,7 +7,7 @@
 // With P = softmax(scale q k^T) recomputed from the saved natural-log LSE:
 //     delta_i = sum_d dout_id out_id          (bwd_delta_kernel)
 //     dS = P * (dout v^T - delta)
-//     dq = scale dS k                         (bwd_dq_kernel: one workgroup per
+//     dq = scale dS k                         (bwd_dq_slot_kernel: one workgroup per
 //                                              128 query rows, walks the keys)
 //     dk = scale dS^T q,  dv = P^T dout       (bwd_dkdv_kernel: one workgroup per
 //                                              128 keys, walks the queries)
@@ -94,17 +94,28 @@ __device__ __forceinline__ void store_zero_rows_bf16(void* base, int64_t row, in
 }
 
 // ------------------------------------------------------------------ dq
-// Workgroup = (128-query tile, h, b); 4 waves x 32 query rows.  Walks the valid
+// Workgroup = (128-query tile, h, b); 4 waves x 32 query rows, walking the valid
 // key tiles with K and V double-buffered in LDS (the next pair is loaded while
-// the current one is used).
+// the current one is used).  Each key tile is split into its two 32-key halves so
+// that the softmax of one half runs on the VALU while the MFMA pipe works on the
+// other: phase A issues S^T and dP^T of keys 0..31; phase B those of keys
+// 32..63 while P and dS of keys 0..31 are formed; phase C accumulates
+// dQ^T += K^T dS^T over keys 0..31 while P and dS of keys 32..63 are formed;
+// phase D accumulates over keys 32..63.  Fixed slots separated by scheduling
+// fences, with the next tiles' DMA spread over the first slots.
 template <int D, int WPE>
 __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads), amdgpu_waves_per_eu(WPE, WPE)))
-void bwd_dq_kernel(BwdArgs a) {
+void bwd_dq_slot_kernel(BwdArgs a) {
   using P = Bf16Dma<D>;
+  constexpr int R = 2;                 // operand reads issued this many slots ahead
+  constexpr int NH = 2 * P::NQ;        // S^T and dP^T MFMAs of one 32-key half
+  constexpr int NC = (D / 32) * 2;     // dQ^T MFMAs of one 32-key half (two 16-key steps)
+  constexpr int EB = (16 + NH - 1) / NH;  // softmax elements per phase B slot (16 per half)
+  constexpr int EC = (16 + NC - 1) / NC;  // per phase C slot
   __shared__ __attribute__((aligned(16))) char smem_raw[P::LDS_BYTES];
   lds_char* const smem = (lds_char*)smem_raw;
-  auto kb_ = [&](int i) { return smem + i * P::TILE_BYTES; };        // K buffers 0, 1
-  auto vb_ = [&](int i) { return smem + (2 + i) * P::TILE_BYTES; };  // V buffers 0, 1
+  auto kb_ = [&](int i) { return smem + i * P::TILE_BYTES; };
+  auto vb_ = [&](int i) { return smem + (2 + i) * P::TILE_BYTES; };
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
@@ -120,7 +131,7 @@ void bwd_dq_kernel(BwdArgs a) {
   const int row = qt * kBM + wave * 32 + (lane & 31);
   const bool row_ok = row < a.Tq;
   const int64_t grow = bh * a.Tq + row;
-  if (n == 0) {  // no valid key: the output is the constant 0
+  if (n == 0) {
     if (row_ok) store_zero_rows_bf16<D>(a.dq, grow, h_half);
     return;
   }
@@ -138,7 +149,7 @@ void bwd_dq_kernel(BwdArgs a) {
   const int64_t src_row = bh * a.Tq + (row_ok ? row : 0);
   P::load_q(qf, reinterpret_cast<const uint16_t*>(a.q) + src_row * D, row_ok, h_half);
   P::load_q(gf, reinterpret_cast<const uint16_t*>(a.dout) + src_row * D, row_ok, h_half);
-  const float L = row_ok ? a.lse[grow] * kLog2e : 0.0f;  // rows past Tq compute finite junk, never stored
+  const float L = row_ok ? a.lse[grow] * kLog2e : 0.0f;
   const float dl = row_ok ? a.delta[grow] : 0.0f;
   const float c = a.scale_log2;
   const int kbase = P::k_base(lane);
@@ -150,35 +161,93 @@ void bwd_dq_kernel(BwdArgs a) {
 
   P::dma_tile(k_tile(0), kb_(0), wave_u, lane);
   P::dma_tile(v_tile(0), vb_(0), wave_u, lane);
-  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+  __builtin_amdgcn_s_waitcnt(0x0F70);
   __syncthreads();
   for (int t = 0; t < T; ++t) {
     const int cur = t & 1;
-    if (t + 1 < T) {  // the other buffers were last read before the previous barrier
-      P::dma_tile(k_tile(t + 1), kb_(cur ^ 1), wave_u, lane);
-      P::dma_tile(v_tile(t + 1), vb_(cur ^ 1), wave_u, lane);
-    }
-    f32x16 s[kBN / 32], dp[kBN / 32];
-    P::scores_vgpr(s, qf, kb_(cur), kbase);   // S^T = K Q^T
-    P::scores_vgpr(dp, gf, vb_(cur), kbase);  // dP^T = V dO^T
-    xdl_result_guard();
+    const lds_char* kt = kb_(cur);
+    const lds_char* vt = vb_(cur);
+    // past the last tile the resources are empty: the loads zero-fill a buffer never read
+    const __amdgpu_buffer_rsrc_t k_rs = k_tile(t + 1), v_rs = v_tile(t + 1);
     const int nv = nv_of(t);
-    u32x4 pk[kBN / 16];
+    f32x16 s[2], dp[2];
+    u32x4 pk[4];
+    float d8[8];
+    // slot j of phases A and B: MFMA j of half `hf`: j even -> S^T (A = K rows), odd -> dP^T (A = V rows)
+    auto frag_ab = [&](int hf, int j) {
+      const int kk = j >> 1;
+      return P::k_frag((j & 1) ? vt : kt, kbase, 2 * kk + hf);
+    };
+    auto mfma_ab = [&](int hf, int j, bf16x8 fr) {
+      const int kk = j >> 1;
+      f32x16& d = (j & 1) ? dp[hf] : s[hf];
+      if (kk == 0) mfma_vgpr_first(d, fr, (j & 1) ? gf.v[0] : qf.v[0]);
+      else mfma_vgpr_acc(d, fr, (j & 1) ? gf.v[kk] : qf.v[kk]);
+    };
+    // softmax element e (0..15) of half hf: register e of S^T block hf
+    auto elem = [&](int hf, int e) {
+      float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[hf][e], c, -L));
+      if (st_key(hf, e, h_half) >= nv) p = 0.0f;
+      d8[e & 7] = p * (dp[hf][e] - dl);
+      if ((e & 7) == 7)
+        pk[2 * hf + (e >> 3)] = u32x4{pack_bf16x2(d8[0], d8[1]), pack_bf16x2(d8[2], d8[3]),
+                                      pack_bf16x2(d8[4], d8[5]), pack_bf16x2(d8[6], d8[7])};
+    };
+    // slot j of phases C and D: dQ^T block db = j % (D/32), 16-key step ks = 2 hf + j / (D/32)
+    auto frag_cd = [&](int hf, int j) { return P::v_frag(kt, vbase, (2 * hf + j / (D / 32)) * (D / 32) + j % (D / 32)); };
+    auto mfma_cd = [&](int hf, int j, bf16x8 fr) {
+      const int db = j % (D / 32), ks = 2 * hf + j / (D / 32);
+      acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr, __builtin_bit_cast(bf16x8, pk[ks]), acc[db], 0, 0, 0);
+    };
+
+    bf16x8 fr[R];
+    // phase A: S^T, dP^T of keys 0..31, with the next tiles' DMA
 #pragma unroll
-    for (int ks = 0; ks < kBN / 16; ++ks) {
-      float d8[8];
+    for (int i = 0; i < R; ++i) fr[i] = frag_ab(0, i);
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int kb = ks >> 1, r = 8 * (ks & 1) + e;
-        float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][r], c, -L));
-        if (st_key(kb, r, h_half) >= nv) p = 0.0f;  // keys past n_b in the last tile
-        d8[e] = p * (dp[kb][r] - dl);
+    for (int j = 0; j < NH; ++j) {
+      mfma_ab(0, j, fr[j % R]);
+      if (j + R < NH) fr[j % R] = frag_ab(0, j + R);
+      else fr[j % R] = frag_ab(1, j + R - NH);
+      if (j < 2 * P::DMA_PER_WAVE) {
+        if (j < P::DMA_PER_WAVE) P::dma_block(k_rs, kb_(cur ^ 1), wave_u, lane, j);
+        else P::dma_block(v_rs, vb_(cur ^ 1), wave_u, lane, j - P::DMA_PER_WAVE);
       }
-      pk[ks] = u32x4{pack_bf16x2(d8[0], d8[1]), pack_bf16x2(d8[2], d8[3]), pack_bf16x2(d8[4], d8[5]),
-                     pack_bf16x2(d8[6], d8[7])};
+      __builtin_amdgcn_sched_barrier(0);
     }
-    P::accumulate(acc, pk, kb_(cur), vbase);  // dQ^T += K^T dS^T
-    __builtin_amdgcn_s_waitcnt(0x0F70);       // the next tiles have landed in LDS
+    xdl_result_guard();  // the softmax below reads the half-0 results
+    // phase B: S^T, dP^T of keys 32..63; P and dS of keys 0..31
+#pragma unroll
+    for (int j = 0; j < NH; ++j) {
+      mfma_ab(1, j, fr[j % R]);
+      if (j + R < NH) fr[j % R] = frag_ab(1, j + R);
+      else fr[j % R] = frag_cd(0, j + R - NH);
+#pragma unroll
+      for (int u = 0; u < EB; ++u)
+        if (j * EB + u < 16) elem(0, j * EB + u);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    xdl_result_guard();  // the softmax below reads the half-1 results
+    // phase C: dQ^T over keys 0..31; P and dS of keys 32..63
+#pragma unroll
+    for (int j = 0; j < NC; ++j) {
+      mfma_cd(0, j, fr[j % R]);
+      if (j + R < NC) fr[j % R] = frag_cd(0, j + R);
+      else fr[j % R] = frag_cd(1, j + R - NC);
+#pragma unroll
+      for (int u = 0; u < EC; ++u)
+        if (j * EC + u < 16) elem(1, j * EC + u);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    // phase D: dQ^T over keys 32..63
+#pragma unroll
+    for (int j = 0; j < NC; ++j) {
+      mfma_cd(1, j, fr[j % R]);
+      if (j + R < NC) fr[j % R] = frag_cd(1, j + R);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // the next tiles have landed in LDS
     lds_barrier();
   }
   if (row_ok) store_rows_bf16<D>(a.dq, grow, acc, a.scale, h_half);

@@ -112,11 +112,12 @@ __device__ __forceinline__ void mfma_vgpr_acc(f32x16& d, bf16x8 a, bf16x8 b) {
   asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(d) : "v"(a), "v"(b));
 }
 
-// 16 wait states between the last of those MFMAs and any VALU read of their
-// results; the scheduling fences keep the compiler from moving work across.
+// 24 wait states between the last of those MFMAs and any VALU read of their
+// results (about twice what a 32x32x16 MFMA needs); the scheduling fences keep
+// the compiler from moving work across.
 __device__ __forceinline__ void xdl_result_guard() {
   __builtin_amdgcn_sched_barrier(0);
-  asm volatile("s_nop 7\n\ts_nop 7" ::: "memory");
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
   __builtin_amdgcn_sched_barrier(0);
 }
 
