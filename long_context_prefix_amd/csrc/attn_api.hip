@@ -95,7 +95,8 @@ attn_status_t dispatch_fwd(const FwdArgs& a, int D, attn_dtype_t dtype, int64_t 
   return ATTN_ERR_UNSUPPORTED;
 }
 
-// WPE_DKDV = 0 selects the software-pipelined dk/dv kernel (one wave per SIMD).
+// WPE_DKDV = 0 selects the cross-tile pipelined dk/dv kernel (one wave per SIMD), otherwise
+// the slotted one at WPE_DKDV waves per SIMD.
 template <int D, int WPE_DQ, int WPE_DKDV>
 attn_status_t launch_bwd(const BwdArgs& base, int64_t rows, int64_t grid_dq, int64_t grid_dkdv, hipStream_t s) {
   (void)hipGetLastError();
@@ -112,7 +113,7 @@ attn_status_t launch_bwd(const BwdArgs& base, int64_t rows, int64_t grid_dq, int
     if constexpr (WPE_DKDV == 0)
       hipLaunchKernelGGL((bwd_dkdv_pipe_kernel<D>), dim3((unsigned)grid_dkdv), dim3(kThreads), 0, s, a);
     else
-      hipLaunchKernelGGL((bwd_dkdv_kernel<D, WPE_DKDV>), dim3((unsigned)grid_dkdv), dim3(kThreads), 0, s, a);
+      hipLaunchKernelGGL((bwd_dkdv_slot_kernel<D, WPE_DKDV>), dim3((unsigned)grid_dkdv), dim3(kThreads), 0, s, a);
   }
   return hipGetLastError() == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
 }

@@ -9,7 +9,7 @@
 //     dS = P * (dout v^T - delta)
 //     dq = scale dS k                         (bwd_dq_slot_kernel: one workgroup per
 //                                              128 query rows, walks the keys)
-//     dk = scale dS^T q,  dv = P^T dout       (bwd_dkdv_kernel: one workgroup per
+//     dk = scale dS^T q,  dv = P^T dout       (bwd_dkdv_*_kernel: one workgroup per
 //                                              128 keys, walks the queries)
 // No atomics: every gradient element is written once, so results are
 // deterministic.  Both walking kernels reuse the forward's 64-row LDS tile
@@ -257,17 +257,29 @@ void bwd_dq_slot_kernel(BwdArgs a) {
 // Workgroup = (128-key block, h, b); 4 waves x 32 keys, each lane owning one key
 // row whose k and v stay in registers.  Walks every query tile (64 rows) with Q,
 // dO and the tile's LSE / delta double-buffered in LDS.  Key rows at or past n_b
-// are written as zeros.
+// are written as zeros.  Each query tile is split into its two 32-query halves,
+// laid out in fixed slots: phase A issues S and dP of
+// queries 0..31 (and the next tiles' DMA); phase B those of queries 32..63
+// while P and dS of queries 0..31 are formed; phase C accumulates dV and dK
+// over queries 0..31 while P and dS of queries 32..63 are formed; phase D
+// accumulates over queries 32..63.  Nothing beyond one tile's scores is held,
+// so this fits D = 256 at one wave per SIMD (D = 128 uses the cross-tile
+// pipelined kernel below, 2% faster there).
 template <int D, int WPE>
 __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads), amdgpu_waves_per_eu(WPE, WPE)))
-void bwd_dkdv_kernel(BwdArgs a) {
+void bwd_dkdv_slot_kernel(BwdArgs a) {
   using P = Bf16Dma<D>;
   constexpr int kKeysPerWg = 128;
+  constexpr int R = 2;
+  constexpr int NH = 2 * P::NQ;           // S and dP MFMAs of one 32-query half
+  constexpr int NC = 2 * (D / 32) * 2;    // dV and dK MFMAs of one half (two 16-query steps each)
+  constexpr int EB = (16 + NH - 1) / NH;  // softmax elements per phase B slot
+  constexpr int EC = (16 + NC - 1) / NC;  // per phase C slot
   __shared__ __attribute__((aligned(16))) char smem_raw[P::LDS_BYTES];
   __shared__ __attribute__((aligned(16))) float stat[2][2][kBN];  // [buffer][lse*log2e | delta][query]
   lds_char* const smem = (lds_char*)smem_raw;
-  auto qb_ = [&](int i) { return smem + i * P::TILE_BYTES; };        // Q buffers 0, 1
-  auto gb_ = [&](int i) { return smem + (2 + i) * P::TILE_BYTES; };  // dO buffers 0, 1
+  auto qb_ = [&](int i) { return smem + i * P::TILE_BYTES; };
+  auto gb_ = [&](int i) { return smem + (2 + i) * P::TILE_BYTES; };
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
@@ -281,10 +293,10 @@ void bwd_dkdv_kernel(BwdArgs a) {
   n = n < 0 ? 0 : (n > a.S ? a.S : n);
   const int64_t bh = (int64_t)b * a.H + h;
   const int key = kblk * kKeysPerWg + wave * 32 + (lane & 31);
-  const bool key_in = key < a.S;  // an allocated slot (its gradient row is written)
-  const bool key_ok = key < n;    // a valid key
+  const bool key_in = key < a.S;
+  const bool key_ok = key < n;
   const int64_t krow = bh * a.S + key;
-  if (kblk * kKeysPerWg >= n || a.Tq == 0) {  // no valid key here, or no query: zero gradients
+  if (kblk * kKeysPerWg >= n || a.Tq == 0) {
     if (key_in) {
       store_zero_rows_bf16<D>(a.dk, krow, h_half);
       store_zero_rows_bf16<D>(a.dv, krow, h_half);
@@ -302,8 +314,6 @@ void bwd_dkdv_kernel(BwdArgs a) {
   auto g_tile = [&](int t) { return make_rsrc(gg + (int64_t)t * kBN * D, (uint32_t)nq_of(t) * (D * 2)); };
   const float* lse_bh = a.lse + bh * a.Tq;
   const float* del_bh = a.delta + bh * a.Tq;
-  // threads 0..63 stage lse * log2e, threads 64..127 delta, for one query tile; queries
-  // past Tq get lse = +inf (so P = 0) and delta = 0
   auto stat_load = [&](int t) -> float {
     const int qi = t * kBN + (tid & 63);
     if (tid < 64) return qi < a.Tq ? lse_bh[qi] * kLog2e : __builtin_inff();
@@ -332,48 +342,115 @@ void bwd_dkdv_kernel(BwdArgs a) {
     const float x = stat_load(0);
     if (tid < 128) stat[0][tid >> 6][tid & 63] = x;
   }
-  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+  __builtin_amdgcn_s_waitcnt(0x0F70);
   __syncthreads();
   for (int t = 0; t < TQ; ++t) {
     const int cur = t & 1;
-    float next_stat = 0.0f;
-    if (t + 1 < TQ) {
-      P::dma_tile(q_tile(t + 1), qb_(cur ^ 1), wave_u, lane);
-      P::dma_tile(g_tile(t + 1), gb_(cur ^ 1), wave_u, lane);
-      next_stat = stat_load(t + 1);
-    }
-    f32x16 s[kBN / 32], dp[kBN / 32];
-    P::scores_vgpr(s, kf, qb_(cur), kbase);   // S = Q K^T   (rows: queries of the tile, lane: key)
-    P::scores_vgpr(dp, vf, gb_(cur), kbase);  // dP = dO V^T
-    xdl_result_guard();
-    u32x4 ppk[kBN / 16], dpk[kBN / 16];
-#pragma unroll
-    for (int ks = 0; ks < kBN / 16; ++ks) {
-      const int kb = ks >> 1;
-      float p8[8], d8[8];
-#pragma unroll
-      for (int g4 = 0; g4 < 2; ++g4) {
-        // registers 8 (ks & 1) + 4 g4 + i hold queries 32 kb + 8 (2 (ks & 1) + g4) + 4 h + i
-        const int q0 = 32 * kb + 8 * (2 * (ks & 1) + g4) + 4 * h_half;
-        const f32x4 Lq = *reinterpret_cast<const f32x4*>(&stat[cur][0][q0]);
-        const f32x4 Dq = *reinterpret_cast<const f32x4*>(&stat[cur][1][q0]);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int r = 8 * (ks & 1) + 4 * g4 + i;
-          const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][r], c, -Lq[i]));
-          p8[4 * g4 + i] = p;
-          d8[4 * g4 + i] = p * (dp[kb][r] - Dq[i]);
-        }
+    const lds_char* qt_ = qb_(cur);
+    const lds_char* gt_ = gb_(cur);
+    // past the last tile the resources are empty: the loads zero-fill a buffer never read
+    const __amdgpu_buffer_rsrc_t q_rs = q_tile(t + 1), g_rs = g_tile(t + 1);
+    const float next_stat = stat_load(t + 1);
+    f32x16 s[2], dp[2];
+    u32x4 ppk[4], dpk[4];
+    float p8[8], d8[8];
+    f32x4 Lq[2], Dq[2];  // statistics of four queries, a ring of two groups
+    auto stat4 = [&](int g, int which) {  // group g of 4 queries: 8 g' + 4 h + i within half g / 4
+      const int q0 = 32 * (g >> 2) + 8 * (g & 3) + 4 * h_half;
+      return *reinterpret_cast<const f32x4*>(&stat[cur][which][q0]);
+    };
+    auto frag_ab = [&](int hf, int j) {  // j even: S (A = Q rows), odd: dP (A = dO rows)
+      return P::k_frag((j & 1) ? gt_ : qt_, kbase, 2 * (j >> 1) + hf);
+    };
+    auto mfma_ab = [&](int hf, int j, bf16x8 fr) {
+      const int kk = j >> 1;
+      f32x16& d = (j & 1) ? dp[hf] : s[hf];
+      if (kk == 0) mfma_vgpr_first(d, fr, (j & 1) ? vf.v[0] : kf.v[0]);
+      else mfma_vgpr_acc(d, fr, (j & 1) ? vf.v[kk] : kf.v[kk]);
+    };
+    // element e (0..15) of half hf: register e of block hf, query 32 hf + 8 (e / 4) + 4 h + e % 4
+    auto elem = [&](int hf, int e) {
+      const int g = 4 * hf + (e >> 2);
+      if ((e & 3) == 0 && (e >> 2) + 1 < 4) {  // fetch the next group of the same half
+        Lq[(g + 1) & 1] = stat4(g + 1, 0);
+        Dq[(g + 1) & 1] = stat4(g + 1, 1);
       }
-      ppk[ks] = u32x4{pack_bf16x2(p8[0], p8[1]), pack_bf16x2(p8[2], p8[3]), pack_bf16x2(p8[4], p8[5]),
-                      pack_bf16x2(p8[6], p8[7])};
-      dpk[ks] = u32x4{pack_bf16x2(d8[0], d8[1]), pack_bf16x2(d8[2], d8[3]), pack_bf16x2(d8[4], d8[5]),
-                      pack_bf16x2(d8[6], d8[7])};
+      const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[hf][e], c, -Lq[g & 1][e & 3]));
+      p8[e & 7] = p;
+      d8[e & 7] = p * (dp[hf][e] - Dq[g & 1][e & 3]);
+      if ((e & 7) == 7) {
+        const int ks = 2 * hf + (e >> 3);
+        ppk[ks] = u32x4{pack_bf16x2(p8[0], p8[1]), pack_bf16x2(p8[2], p8[3]), pack_bf16x2(p8[4], p8[5]),
+                        pack_bf16x2(p8[6], p8[7])};
+        dpk[ks] = u32x4{pack_bf16x2(d8[0], d8[1]), pack_bf16x2(d8[2], d8[3]), pack_bf16x2(d8[4], d8[5]),
+                        pack_bf16x2(d8[6], d8[7])};
+      }
+    };
+    // slot j of phases C and D: j even -> dV (A = dO^T, B = P), odd -> dK (A = Q^T, B = dS);
+    // m = j / 2 walks (16-query step ks = 2 hf + m / (D/32), block db = m % (D/32))
+    auto frag_cd = [&](int hf, int j) {
+      const int m = j >> 1;
+      return P::v_frag((j & 1) ? qt_ : gt_, vbase, (2 * hf + m / (D / 32)) * (D / 32) + m % (D / 32));
+    };
+    auto mfma_cd = [&](int hf, int j, bf16x8 fr) {
+      const int m = j >> 1, db = m % (D / 32), ks = 2 * hf + m / (D / 32);
+      if (j & 1) dk[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr, __builtin_bit_cast(bf16x8, dpk[ks]), dk[db], 0, 0, 0);
+      else dv[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr, __builtin_bit_cast(bf16x8, ppk[ks]), dv[db], 0, 0, 0);
+    };
+
+    bf16x8 fr[R];
+#pragma unroll
+    for (int i = 0; i < R; ++i) fr[i] = frag_ab(0, i);
+    Lq[0] = stat4(0, 0);
+    Dq[0] = stat4(0, 1);
+    __builtin_amdgcn_sched_barrier(0);
+    // phase A: S, dP of queries 0..31, and the next tiles' DMA
+#pragma unroll
+    for (int j = 0; j < NH; ++j) {
+      mfma_ab(0, j, fr[j % R]);
+      if (j + R < NH) fr[j % R] = frag_ab(0, j + R);
+      else fr[j % R] = frag_ab(1, j + R - NH);
+      if (j < 2 * P::DMA_PER_WAVE) {
+        if (j < P::DMA_PER_WAVE) P::dma_block(q_rs, qb_(cur ^ 1), wave_u, lane, j);
+        else P::dma_block(g_rs, gb_(cur ^ 1), wave_u, lane, j - P::DMA_PER_WAVE);
+      }
+      __builtin_amdgcn_sched_barrier(0);
     }
-    P::accumulate(dv, ppk, gb_(cur), vbase);  // dV^T += dO^T P
-    P::accumulate(dk, dpk, qb_(cur), vbase);  // dK^T += Q^T dS
-    if (t + 1 < TQ && tid < 128) stat[cur ^ 1][tid >> 6][tid & 63] = next_stat;
-    __builtin_amdgcn_s_waitcnt(0x0F70);  // the next tiles have landed in LDS
+    xdl_result_guard();
+    // phase B: S, dP of queries 32..63; P, dS of queries 0..31
+#pragma unroll
+    for (int j = 0; j < NH; ++j) {
+      mfma_ab(1, j, fr[j % R]);
+      if (j + R < NH) fr[j % R] = frag_ab(1, j + R);
+      else fr[j % R] = frag_cd(0, j + R - NH);
+#pragma unroll
+      for (int u = 0; u < EB; ++u)
+        if (j * EB + u < 16) elem(0, j * EB + u);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    Lq[0] = stat4(4, 0);  // group 4 opens the second half
+    Dq[0] = stat4(4, 1);
+    xdl_result_guard();
+    // phase C: dV, dK over queries 0..31; P, dS of queries 32..63
+#pragma unroll
+    for (int j = 0; j < NC; ++j) {
+      mfma_cd(0, j, fr[j % R]);
+      if (j + R < NC) fr[j % R] = frag_cd(0, j + R);
+      else fr[j % R] = frag_cd(1, j + R - NC);
+#pragma unroll
+      for (int u = 0; u < EC; ++u)
+        if (j * EC + u < 16) elem(1, j * EC + u);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    // phase D: dV, dK over queries 32..63
+#pragma unroll
+    for (int j = 0; j < NC; ++j) {
+      mfma_cd(1, j, fr[j % R]);
+      if (j + R < NC) fr[j % R] = frag_cd(1, j + R);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    if (tid < 128) stat[cur ^ 1][tid >> 6][tid & 63] = next_stat;
+    __builtin_amdgcn_s_waitcnt(0x0F70);
     lds_barrier();
   }
   if (key_in) {
@@ -388,7 +465,8 @@ void bwd_dkdv_kernel(BwdArgs a) {
 }
 
 // ---------------------------------------------------- dk, dv (pipelined)
-// The same computation at one wave per SIMD with the loop software-pipelined:
+// The same computation at one wave per SIMD with the loop software-pipelined
+// across tiles:
 // iteration t issues S_{t+1} = Q_{t+1} K^T and dP_{t+1} = dO_{t+1} V^T on the
 // MFMA pipe while the VALU turns S_t, dP_t into P_t and dS_t, then accumulates
 // dV += dO_t^T P_t and dK += Q_t^T dS_t.  Q and dO tiles are triple-buffered
