@@ -104,6 +104,28 @@ attn_status_t attn_splitkv_partial(const void* q, const void* k, const void* v, 
                                    int B, int H, int Tq, int S, int D, float scale, attn_dtype_t dtype,
                                    int chunk, float* part_out, float* part_lse, void* stream);
 
+/* Split-KV in one launch: the partials of attn_splitkv_partial, then, inside the
+ * same kernel, the merge of attn_lse_combine done by the last of the C chunk
+ * workgroups of each (b, h, 128-query tile) to finish -- the partial results
+ * merged with their log-sum-exp weights (tabfm PR #81, section
+ * Sequence-parallel inference), without a second launch.
+ *   part_out, part_lse : as for attn_splitkv_partial (caller-provided scratch;
+ *                        every element is written)
+ *   counters : device int32 [B, H, ceil(Tq / 128)]; must be all zero before the
+ *              first call; every call leaves it all zero again.  Calls that share
+ *              a counters buffer must not run concurrently.
+ *   out, lse : as for attn_lse_combine, out in `dtype` (lse may be NULL)
+ * The merged result is bit-identical to attn_splitkv_partial followed by
+ * attn_lse_combine.  On MI355X it is slower than those two calls (10.7 ms vs
+ * 6.3 ms on 160 x 4 heads x 100,000 keys): each chunk's device-scope release
+ * writes back its XCD's L2, which costs more than the second launch it saves.
+ * Errors as for attn_splitkv_partial, plus ATTN_ERR_NULLPTR
+ * (counters or out NULL) and ATTN_ERR_ALIGN (counters/lse not 4-byte aligned,
+ * out not 16-byte aligned). */
+attn_status_t attn_splitkv_fwd(const void* q, const void* k, const void* v, const int32_t* kv_len, int B, int H,
+                               int Tq, int S, int D, float scale, attn_dtype_t dtype, int chunk, float* part_out,
+                               float* part_lse, int32_t* counters, void* out, float* lse, void* stream);
+
 /* Exact log-sum-exp merge of C partials (tabfm PR #81, section
  * Sequence-parallel inference): with M = max_c L_c,
  *     M = -inf  ->  out = 0, lse = -inf

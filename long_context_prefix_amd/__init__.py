@@ -7,6 +7,8 @@ The public calls mirror the C ABI of ``libattnprefix.so``:
 * ``attn_splitkv_partial(q, k, v, kv_len, chunk, scale)`` -- fp32 partials
   over fixed key chunks;
 * ``attn_lse_combine(part_out, part_lse)`` -- their exact log-sum-exp merge;
+* ``attn_splitkv_fwd(q, k, v, kv_len, chunk)`` -- both in one launch (the last
+  chunk to finish merges);
 * ``attn_prefix_mask_to_kv_len(mask)`` / ``sdpa_prefix(q, k, v, attn_mask)`` --
   a [B, 1, 1, S] boolean prefix mask turned into lengths on the device, and an
   SDPA-style entry that raises on any other mask;
@@ -23,6 +25,7 @@ from ._lib import (  # noqa: F401
     attn_prefix_bwd,
     attn_prefix_fwd,
     attn_prefix_mask_to_kv_len,
+    attn_splitkv_fwd,
     attn_splitkv_num_chunks,
     attn_splitkv_partial,
     kv_len_from_prefix_mask,

@@ -23,7 +23,7 @@ STATUS_NAMES = {
     5: "ATTN_ERR_ALIGN", 6: "ATTN_ERR_CHUNK", 7: "ATTN_ERR_HIP", 8: "ATTN_ERR_ARG",
 }
 ATTN_BF16, ATTN_F32 = 0, 1
-EXPORTED = ("attn_version", "attn_prefix_fwd", "attn_splitkv_partial", "attn_lse_combine",
+EXPORTED = ("attn_version", "attn_prefix_fwd", "attn_splitkv_partial", "attn_lse_combine", "attn_splitkv_fwd",
             "attn_prefix_mask_to_kv_len", "attn_prefix_bwd", "attn_splitkv_num_chunks", "attn_status_string")
 
 _lib = None
@@ -55,6 +55,8 @@ def load() -> ctypes.CDLL:
     L.attn_lse_combine.argtypes = [vp, vp, i32, i32, i32, i32, i32, i32, vp, vp, vp]
     L.attn_prefix_mask_to_kv_len.restype = i32
     L.attn_prefix_mask_to_kv_len.argtypes = [vp, i32, i32, ctypes.c_int64, vp, vp]
+    L.attn_splitkv_fwd.restype = i32
+    L.attn_splitkv_fwd.argtypes = [vp, vp, vp, vp, i32, i32, i32, i32, i32, f32, i32, i32, vp, vp, vp, vp, vp, vp]
     L.attn_prefix_bwd.restype = i32
     L.attn_prefix_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, f32, i32, vp, vp, vp, vp, vp]
     L.attn_splitkv_num_chunks.restype = i32
@@ -299,3 +301,49 @@ def prefix_attention(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, kv_len: 
                      scale: Optional[float] = None) -> torch.Tensor:
     """Differentiable prefix-masked attention (forward and backward on the HIP kernels)."""
     return _PrefixAttention.apply(q, k, v, kv_len, scale)
+
+
+def attn_splitkv_fwd(q, k, v, kv_len, chunk: int, scale: Optional[float] = None,
+                     part_out: Optional[torch.Tensor] = None, part_lse: Optional[torch.Tensor] = None,
+                     counters: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None,
+                     lse: Optional[torch.Tensor] = None, return_lse: bool = True):
+    """Split-KV partials and their merge in one launch; returns (out, lse).
+
+    ``counters`` (int32 [B, H, ceil(Tq/128)]) must be zero before the call and is
+    zero again after it; it is allocated when not given.
+    """
+    B, H, Tq, S, D, dev = _fwd_shapes(q, k, v, kv_len)
+    scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
+    if chunk <= 0:
+        raise ValueError("chunk must be positive")
+    C = -(-S // chunk)
+    if part_out is None:
+        part_out = torch.empty((B, H, C, Tq, D), dtype=torch.float32, device=dev)
+    if part_lse is None:
+        part_lse = torch.empty((B, H, C, Tq), dtype=torch.float32, device=dev)
+    nqt = -(-Tq // 128)
+    if counters is None:
+        counters = torch.zeros((B, H, nqt), dtype=torch.int32, device=dev)
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None and return_lse:
+        lse = torch.empty((B, H, Tq), dtype=torch.float32, device=dev)
+    for t, name in ((part_out, "part_out"), (part_lse, "part_lse"), (counters, "counters"), (out, "out")):
+        _require(t, name, dev)
+    if part_out.shape != (B, H, C, Tq, D) or part_lse.shape != (B, H, C, Tq):
+        raise ValueError("partial buffers have the wrong shape")
+    if part_out.dtype != torch.float32 or part_lse.dtype != torch.float32:
+        raise ValueError("partial buffers must be fp32")
+    if counters.dtype != torch.int32 or counters.shape != (B, H, nqt):
+        raise ValueError("counters must be int32 [B, H, ceil(Tq / 128)]")
+    if out.shape != q.shape or out.dtype != q.dtype:
+        raise ValueError("out must match q in shape and dtype")
+    if lse is not None:
+        _require(lse, "lse", dev)
+        if lse.shape != (B, H, Tq) or lse.dtype != torch.float32:
+            raise ValueError("lse must be fp32 [B, H, Tq]")
+    code = load().attn_splitkv_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(kv_len), B, H, Tq, S, D, scale, _dtype_code(q),
+                                   int(chunk), _ptr(part_out), _ptr(part_lse), _ptr(counters), _ptr(out), _ptr(lse),
+                                   _stream(dev))
+    _check("attn_splitkv_fwd", code)
+    return out, lse

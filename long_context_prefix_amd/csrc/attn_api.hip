@@ -57,7 +57,7 @@ attn_status_t check_fwd(const void* q, const void* k, const void* v, const int32
   return ATTN_OK;
 }
 
-template <class P, int D, bool PARTIAL, int W>
+template <class P, int D, bool PARTIAL, int W, bool MERGE>
 attn_status_t launch_fwd(const FwdArgs& a, int64_t grid, hipStream_t stream, const char* tag) {
   // one query tile per head: every K/V tile is read by one workgroup, so stream it
   const bool stream_kv = !P::kIsF32 && a.n_qtiles == 1;
@@ -67,29 +67,30 @@ attn_status_t launch_fwd(const FwdArgs& a, int64_t grid, hipStream_t stream, con
   (void)hipGetLastError();  // clear an error left by unrelated earlier calls
   if constexpr (!P::kIsF32) {
     if (stream_kv) {
-      hipLaunchKernelGGL((attn_fwd_kernel<P, D, PARTIAL, W, true>), dim3((unsigned)grid), dim3(kThreads), 0, stream,
-                         a);
+      hipLaunchKernelGGL((attn_fwd_kernel<P, D, PARTIAL, W, true, MERGE>), dim3((unsigned)grid), dim3(kThreads), 0,
+                         stream, a);
       return hipGetLastError() == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
     }
   }
-  hipLaunchKernelGGL((attn_fwd_kernel<P, D, PARTIAL, W, false>), dim3((unsigned)grid), dim3(kThreads), 0, stream, a);
+  hipLaunchKernelGGL((attn_fwd_kernel<P, D, PARTIAL, W, false, MERGE>), dim3((unsigned)grid), dim3(kThreads), 0,
+                     stream, a);
   return hipGetLastError() == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
 }
 
-template <bool PARTIAL>
+template <bool PARTIAL, bool MERGE = false>
 attn_status_t dispatch_fwd(const FwdArgs& a, int D, attn_dtype_t dtype, int64_t grid, hipStream_t s) {
-  const char* tag = PARTIAL ? "splitkv_partial" : "prefix_fwd";
+  const char* tag = MERGE ? "splitkv_fwd" : (PARTIAL ? "splitkv_partial" : "prefix_fwd");
   if (dtype == ATTN_BF16) {
     switch (D) {
-      case 64: return launch_fwd<Bf16Dma<64>, 64, PARTIAL, 2>(a, grid, s, tag);
-      case 128: return launch_fwd<Bf16Dma<128>, 128, PARTIAL, 2>(a, grid, s, tag);
-      case 256: return launch_fwd<Bf16Dma<256>, 256, PARTIAL, 1>(a, grid, s, tag);
+      case 64: return launch_fwd<Bf16Dma<64>, 64, PARTIAL, 2, MERGE>(a, grid, s, tag);
+      case 128: return launch_fwd<Bf16Dma<128>, 128, PARTIAL, 2, MERGE>(a, grid, s, tag);
+      case 256: return launch_fwd<Bf16Dma<256>, 256, PARTIAL, 1, MERGE>(a, grid, s, tag);
     }
   } else {
     switch (D) {
-      case 64: return launch_fwd<F32Path<64>, 64, PARTIAL, 1>(a, grid, s, tag);
-      case 128: return launch_fwd<F32Path<128>, 128, PARTIAL, 1>(a, grid, s, tag);
-      case 256: return launch_fwd<F32Path<256>, 256, PARTIAL, 1>(a, grid, s, tag);
+      case 64: return launch_fwd<F32Path<64>, 64, PARTIAL, 1, MERGE>(a, grid, s, tag);
+      case 128: return launch_fwd<F32Path<128>, 128, PARTIAL, 1, MERGE>(a, grid, s, tag);
+      case 256: return launch_fwd<F32Path<256>, 256, PARTIAL, 1, MERGE>(a, grid, s, tag);
     }
   }
   return ATTN_ERR_UNSUPPORTED;
@@ -259,6 +260,41 @@ attn_status_t attn_splitkv_partial(const void* q, const void* k, const void* v, 
   a.part_lse = part_lse;
   const int64_t grid = (int64_t)a.n_qtiles * C * B * H;
   return dispatch_fwd<true>(a, D, dtype, grid, reinterpret_cast<hipStream_t>(stream));
+}
+
+attn_status_t attn_splitkv_fwd(const void* q, const void* k, const void* v, const int32_t* kv_len, int B, int H,
+                               int Tq, int S, int D, float scale, attn_dtype_t dtype, int chunk, float* part_out,
+                               float* part_lse, int32_t* counters, void* out, float* lse, void* stream) {
+  bool noop = false;
+  attn_status_t st =
+      check_fwd(q, k, v, kv_len, B, H, Tq, S, D, scale, dtype, part_out, part_lse, true, chunk, true, &noop);
+  if (st != ATTN_OK || noop) return st;
+  if (!counters || !out) return ATTN_ERR_NULLPTR;
+  if (!aligned4(counters) || !aligned16(out) || (lse && !aligned4(lse))) return ATTN_ERR_ALIGN;
+  const int C = attn_splitkv_num_chunks(S, chunk);
+  if (C == 0) {  // S == 0: no key at all, so out = 0 and lse = -inf, which the combine writes for C = 0
+    return attn_lse_combine(part_out, part_lse, B, H, 0, Tq, D, dtype, out, lse, stream);
+  }
+  FwdArgs a{};
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.kv_len = kv_len;
+  a.B = B;
+  a.H = H;
+  a.Tq = Tq;
+  a.S = S;
+  a.scale_log2 = scale * kLog2e;
+  a.chunk = chunk;
+  a.C = C;
+  a.n_qtiles = (Tq + kBM - 1) / kBM;
+  a.part_out = part_out;
+  a.part_lse = part_lse;
+  a.counters = counters;
+  a.out = out;
+  a.lse = lse;
+  const int64_t grid = (int64_t)a.n_qtiles * C * B * H;
+  return dispatch_fwd<true, true>(a, D, dtype, grid, reinterpret_cast<hipStream_t>(stream));
 }
 
 attn_status_t attn_lse_combine(const float* part_out, const float* part_lse, int B, int H, int C, int Tq, int D,

@@ -63,6 +63,7 @@ struct FwdArgs {
   float* lse;        // final mode: [B,H,Tq] or null
   float* part_out;   // split mode: [B,H,C,Tq,D]
   float* part_lse;   // split mode: [B,H,C,Tq]
+  int32_t* counters; // single-launch split mode: [B,H,n_qtiles] arrival counts, zero between launches
 };
 
 __device__ __forceinline__ float pair_max(float x) {
@@ -848,19 +849,55 @@ __device__ __forceinline__ void bf16_fwd_dma(const FwdArgs& a, char* smem_generi
   write_rows<P, D, PARTIAL>(a, w, o, 1.0f / l, (sm.m + __builtin_amdgcn_logf(l)) * kLn2, h_half);
 }
 
-template <class P, int D, bool PARTIAL, int WAVES_PER_EU, bool STREAM>
-__global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads), amdgpu_waves_per_eu(WAVES_PER_EU, WAVES_PER_EU)))
-void attn_fwd_kernel(FwdArgs a) {
-  if constexpr (P::kIsF32) {
-    __shared__ __attribute__((aligned(16))) char smem[P::LDS_BYTES];
-    attn_fwd_body<P, D, PARTIAL>(a, smem);
-  } else {
-    __shared__ __attribute__((aligned(16))) char smem[P::LDS_BYTES];
-    bf16_fwd_dma<D, PARTIAL, STREAM>(a, smem);
+// ------------------------------------------------------------ LSE combine
+// Merge of the C partials of one output row, four columns per thread: with
+// M = max_c L_c, w_c = 2^((L_c - M) log2 e), out = sum_c w_c O_c / sum_c w_c and
+// lse = M + ln sum_c w_c; M = -inf gives out = 0, lse = -inf.  pl points at L_0
+// of the row (stride Tq between chunks), po at O_0 of the thread's columns
+// (stride Tq * D).  Shared by the combine kernel and the single-launch split path
+// so that both produce the same bits.
+template <int D, bool OUT_F32>
+__device__ __forceinline__ void merge_row4(const float* pl, const float* po, int C, int Tq, void* out, float* lse,
+                                           int64_t row, int col) {
+  float mx = -__builtin_inff();
+  for (int c = 0; c < C; ++c) mx = fmaxf(mx, pl[(int64_t)c * Tq]);
+
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  float wsum = 0.f;
+  if (mx != -__builtin_inff()) {
+    int c = 0;
+    for (; c + 4 <= C; c += 4) {
+      f32x4 x[4];
+      float lc[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        lc[u] = pl[(int64_t)(c + u) * Tq];
+        x[u] = *reinterpret_cast<const f32x4*>(po + (int64_t)(c + u) * Tq * D);
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const float w = __builtin_amdgcn_exp2f((lc[u] - mx) * kLog2e);
+        wsum += w;
+        acc += w * x[u];
+      }
+    }
+    for (; c < C; ++c) {
+      const float w = __builtin_amdgcn_exp2f((pl[(int64_t)c * Tq] - mx) * kLog2e);
+      wsum += w;
+      acc += w * *reinterpret_cast<const f32x4*>(po + (int64_t)c * Tq * D);
+    }
+    acc *= 1.0f / wsum;
   }
+  const int64_t off = row * D + col;
+  if (OUT_F32) {
+    *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(out) + off) = acc;
+  } else {
+    u32x2 w = {pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3])};
+    *reinterpret_cast<u32x2*>(reinterpret_cast<uint16_t*>(out) + off) = w;
+  }
+  if (lse && col == 0) lse[row] = (mx == -__builtin_inff()) ? mx : mx + __builtin_amdgcn_logf(wsum) * kLn2;
 }
 
-// ------------------------------------------------------------ LSE combine
 // One row (b, h, i) is handled by D/4 consecutive threads, each owning four
 // consecutive output columns; a 256-thread workgroup covers 1024/D rows.
 struct CombineArgs {
@@ -881,46 +918,61 @@ void lse_combine_kernel(CombineArgs a) {
   const int col = (threadIdx.x % TPR) * 4;
   const int64_t bh = row / a.Tq;
   const int i = (int)(row - bh * a.Tq);
-  const float* pl = a.part_lse + bh * a.C * a.Tq + i;       // stride Tq between chunks
+  const float* pl = a.part_lse + bh * a.C * a.Tq + i;              // stride Tq between chunks
   const float* po = a.part_out + (bh * a.C * a.Tq + i) * D + col;  // stride Tq*D between chunks
+  merge_row4<D, OUT_F32>(pl, po, a.C, a.Tq, a.out, a.lse, row, col);
+}
 
-  float mx = -__builtin_inff();
-  for (int c = 0; c < a.C; ++c) mx = fmaxf(mx, pl[(int64_t)c * a.Tq]);
-
-  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-  float wsum = 0.f;
-  if (mx != -__builtin_inff()) {
-    int c = 0;
-    for (; c + 4 <= a.C; c += 4) {
-      f32x4 x[4];
-      float lc[4];
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        lc[u] = pl[(int64_t)(c + u) * a.Tq];
-        x[u] = *reinterpret_cast<const f32x4*>(po + (int64_t)(c + u) * a.Tq * D);
-      }
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const float w = __builtin_amdgcn_exp2f((lc[u] - mx) * kLog2e);
-        wsum += w;
-        acc += w * x[u];
-      }
-    }
-    for (; c < a.C; ++c) {
-      const float w = __builtin_amdgcn_exp2f((pl[(int64_t)c * a.Tq] - mx) * kLog2e);
-      wsum += w;
-      acc += w * *reinterpret_cast<const f32x4*>(po + (int64_t)c * a.Tq * D);
-    }
-    acc *= 1.0f / wsum;
+// Single-launch split-KV: after a chunk's workgroup has written its partial, it
+// counts itself in for its (b, h, query tile); the workgroup that arrives last
+// merges the C partials of that tile's rows (the same arithmetic as the combine
+// kernel) and resets the count to zero for the next launch.  The eight XCDs
+// have separate L2 caches, so the hand-off uses device-scope fences: a release
+// (L2 write-back) before the count, an acquire (L2 invalidate) before the merge
+// reads the other chunks' partials.
+template <int D, bool OUT_F32>
+__device__ __forceinline__ void splitkv_merge_tail(const FwdArgs& a) {
+  __shared__ int s_last;
+  int wg = blockIdx.x;
+  const int qt = wg % a.n_qtiles;
+  wg /= a.n_qtiles;
+  wg /= a.C;
+  const int h = wg % a.H, b = wg / a.H;
+  const int64_t bh = (int64_t)b * a.H + h;
+  const int64_t cidx = bh * a.n_qtiles + qt;
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this thread's partial stores have reached L2
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");  // release at device scope (L2 write-back)
+    s_last = (__hip_atomic_fetch_add(&a.counters[cidx], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == a.C - 1);
   }
-  const int64_t off = row * D + col;
-  if (OUT_F32) {
-    *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(a.out) + off) = acc;
+  __syncthreads();
+  if (!s_last) return;
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");  // acquire (L2 invalidate): every chunk's partial is visible
+  constexpr int TPR = D / 4, RPP = kThreads / TPR;  // threads per row, rows per pass
+  const int col = (threadIdx.x % TPR) * 4;
+  for (int r = threadIdx.x / TPR; r < kBM; r += RPP) {
+    const int i = qt * kBM + r;
+    if (i >= a.Tq) break;
+    const float* pl = a.part_lse + bh * a.C * a.Tq + i;
+    const float* po = a.part_out + (bh * a.C * a.Tq + i) * D + col;
+    merge_row4<D, OUT_F32>(pl, po, a.C, a.Tq, a.out, a.lse, bh * a.Tq + i, col);
+  }
+  if (threadIdx.x == 0) a.counters[cidx] = 0;
+}
+
+template <class P, int D, bool PARTIAL, int WAVES_PER_EU, bool STREAM, bool MERGE = false>
+__global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads), amdgpu_waves_per_eu(WAVES_PER_EU, WAVES_PER_EU)))
+void attn_fwd_kernel(FwdArgs a) {
+  static_assert(!MERGE || PARTIAL, "the merge tail follows a partial");
+  if constexpr (P::kIsF32) {
+    __shared__ __attribute__((aligned(16))) char smem[P::LDS_BYTES];
+    attn_fwd_body<P, D, PARTIAL>(a, smem);
   } else {
-    u32x2 w = {pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3])};
-    *reinterpret_cast<u32x2*>(reinterpret_cast<uint16_t*>(a.out) + off) = w;
+    __shared__ __attribute__((aligned(16))) char smem[P::LDS_BYTES];
+    bf16_fwd_dma<D, PARTIAL, STREAM>(a, smem);
   }
-  if (a.lse && col == 0) a.lse[row] = (mx == -__builtin_inff()) ? mx : mx + __builtin_amdgcn_logf(wsum) * kLn2;
+  if constexpr (MERGE) splitkv_merge_tail<D, P::kIsF32>(a);
 }
 
 // ------------------------------------------------------- prefix mask -> kv_len

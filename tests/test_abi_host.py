@@ -207,3 +207,19 @@ def test_bwd_argument_errors(L):
     assert call(B=0, q=None, k=None, v=None, kv=None, out=None, dout=None, lse=None, delta=None, dq=None, dk=None,
                 dv=None) == OK
     assert call(S=2**23, D=128) == SHAPE  # 2^31 bytes per (b, h) slice
+
+
+def test_single_launch_split_argument_errors(L):
+    def call(counters=P, out=P, lse=None, chunk=64, **kw):
+        a = dict(q=P, k=P, v=P, kv=P, B=1, H=1, Tq=1, S=64, D=64, scale=0.125, dt=BF16, po=P, pl=P)
+        a.update(kw)
+        return L.attn_splitkv_fwd(a["q"], a["k"], a["v"], a["kv"], a["B"], a["H"], a["Tq"], a["S"], a["D"],
+                                  a["scale"], a["dt"], chunk, a["po"], a["pl"], counters, out, lse, None)
+
+    assert call(chunk=96) == CHUNK
+    assert call(counters=None) == NULLPTR
+    assert call(out=None) == NULLPTR
+    assert call(counters=ctypes.c_void_p(4098)) == ALIGN
+    assert call(out=PM) == ALIGN
+    assert call(lse=ctypes.c_void_p(4097)) == ALIGN
+    assert call(B=0, counters=None, out=None) == OK

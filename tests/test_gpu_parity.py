@@ -317,3 +317,32 @@ def test_largest_key_slice():
     o2, l2 = _run_fused(q2, k, v, kv, 0.0625)
     r2o, r2l = ref_prefix_fwd(_np(q2), _np(k[:, :, :n]), _np(v[:, :, :n]), [n], 0.0625)
     assert_parity(o2, l2, r2o, r2l, "bf16", "largest slice, last key")
+
+
+@pytest.mark.parametrize("D,Tq,chunk,dtype", [(64, 1, 64, "bf16"), (128, 129, 128, "bf16"), (256, 300, 192, "bf16"),
+                                              (128, 200, 64, "f32"), (128, 150, 4096, "bf16")])
+def test_splitkv_single_launch(D, Tq, chunk, dtype):
+    """One launch (partials, then the last chunk per query tile merges) gives the same bits as
+    partial + combine, and the oracle's result; partial buffers start as NaN so a merge that
+    read a partial before it was written would show; the counters come back zero."""
+    B, H, S = 3, 2, 700
+    lens = [700, 0, 333]
+    log(f"single-launch split D={D} Tq={Tq} chunk={chunk} {dtype}")
+    q, k, v, kv = make_inputs(B, H, Tq, S, D, lens, dtype, 1.0, seed=4000 + D + Tq, device=DEV)
+    scale = 1.0 / math.sqrt(D)
+    C = -(-S // chunk)
+    po = torch.full((B, H, C, Tq, D), float("nan"), device=DEV)
+    pl = torch.full((B, H, C, Tq), float("nan"), device=DEV)
+    counters = torch.zeros((B, H, -(-Tq // 128)), dtype=torch.int32, device=DEV)
+    for rep in range(2):  # the second call reuses the counters the first one reset
+        po.fill_(float("nan"))
+        pl.fill_(float("nan"))
+        out, lse = _lib.attn_splitkv_fwd(q, k, v, kv, chunk, scale, part_out=po, part_lse=pl, counters=counters)
+        torch.cuda.synchronize()
+        assert int(counters.abs().sum()) == 0, "counters not reset"
+        rpo, rpl = _lib.attn_splitkv_partial(q, k, v, kv, chunk, scale)
+        rout, rlse = _lib.attn_lse_combine(rpo, rpl, q.dtype)
+        torch.cuda.synchronize()
+        assert torch.equal(out, rout) and torch.equal(lse, rlse), f"call {rep}: differs from partial + combine"
+    ro, rl = ref_prefix_fwd(to64(q), to64(k), to64(v), np.array(lens), scale)
+    assert_parity(out, lse, ro, rl, dtype, f"single-launch split D={D}")
