@@ -1,0 +1,81 @@
+"""Host-side logic (CPU only): the input recipe, the product/oracle separation, the
+benchmark's single-GPU contract."""
+
+import ast
+import os
+import subprocess
+import sys
+
+import numpy as np
+import torch
+
+from long_context_prefix_amd.workloads import WORKLOADS, make_inputs, ragged_kv_len, sample_rows
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+PKG = os.path.join(ROOT, "long_context_prefix_amd")
+
+
+def test_pads_sit_exactly_past_each_prefix():
+    lens = [5, 0, 12]
+    q, k, v, kv = make_inputs(3, 2, 4, 12, 64, lens, "bf16", 1.0, seed=7)
+    assert kv.tolist() == lens and kv.dtype == torch.int32
+    for b, n in enumerate(lens):
+        for t in (k, v):
+            pad = t[b, :, n:].float()
+            assert torch.all(pad.abs() == 9984.0), "pads are +-1e4 rounded to bf16"
+            if n:
+                assert torch.all(t[b, :, :n].float().abs() < 100.0)
+    # NaN pads for the invariance tests
+    _, k2, v2, _ = make_inputs(3, 2, 4, 12, 64, lens, "bf16", 1.0, seed=7, pad=float("nan"))
+    assert torch.isnan(k2[0, :, 5:].float()).all() and not torch.isnan(k2[0, :, :5].float()).any()
+    # the valid part does not depend on the pad value
+    assert torch.equal(k2[0, :, :5], k[0, :, :5]) and torch.equal(v2[2, :, :12], v[2, :, :12])
+
+
+def test_inputs_are_reproducible_and_per_sequence_draws_stand_alone():
+    a = make_inputs(2, 1, 3, 8, 64, [8, 3], "f32", 0.5, seed=11)
+    b = make_inputs(2, 1, 3, 8, 64, [8, 3], "f32", 0.5, seed=11)
+    for x, y in zip(a, b):
+        assert torch.equal(x, y)
+    full = make_inputs(3, 1, 2, 8, 64, [8, 4, 2], "bf16", 1.0, seed=3, per_sequence=True)
+    one = make_inputs(1, 1, 2, 8, 64, [4], "bf16", 1.0, seed=3 + 1 + 1, per_sequence=False)
+    # element b of a per-sequence draw is the plain draw seeded seed + 1 + b
+    assert torch.equal(full[0][1:2], one[0]) and torch.equal(full[1][1:2], one[1])
+
+
+def test_ragged_lengths_force_both_ends():
+    lens = ragged_kv_len(1003, 8, 32768)
+    assert lens[0] == 1 and lens[-1] == 32768 and lens.min() >= 1 and lens.max() <= 32768
+    assert np.array_equal(lens, WORKLOADS["ragged_32k"].lens())
+
+
+def test_sampled_rows_hold_both_ends():
+    rows = sample_rows(5, 1000, 17, 4)
+    assert rows.shape == (4, 17)
+    assert np.all(rows[:, 0] == 0) and np.all(rows[:, -1] == 999)
+    assert all(len(set(r.tolist())) == 17 for r in rows)
+
+
+def test_product_never_imports_the_oracle():
+    """Only tests, the smoke check and the benchmark's CPU-baseline leg may use the oracle."""
+    for dirpath, _, files in os.walk(PKG):
+        for f in files:
+            if not f.endswith(".py"):
+                continue
+            tree = ast.parse(open(os.path.join(dirpath, f)).read())
+            for node in ast.walk(tree):
+                names = []
+                if isinstance(node, ast.Import):
+                    names = [a.name for a in node.names]
+                elif isinstance(node, ast.ImportFrom):
+                    names = [node.module or ""]
+                assert not any(n == "oracle" or n.startswith("oracle.") for n in names), f"{f} imports the oracle"
+    for f in os.listdir(os.path.join(PKG, "csrc")):
+        assert "oracle" not in open(os.path.join(PKG, "csrc", f)).read(), f
+
+
+def test_bench_refuses_more_than_one_gpu():
+    res = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"], capture_output=True,
+                         text=True, timeout=120)
+    assert res.returncode == 2
+    assert "one GPU" in res.stderr
