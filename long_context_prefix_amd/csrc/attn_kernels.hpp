@@ -240,24 +240,10 @@ struct Bf16Dma {
     return addr(4 * hv + e, 32 * dh + 8 * jj);
   }
 
-  // S^T (two 32-key blocks) = K_tile Q^T
-  __device__ static void scores(f32x16 (&s)[kBN / 32], const QFrag& f, const lds_char* kt, int kbase) {
-#pragma unroll
-    for (int kb = 0; kb < kBN / 32; ++kb) s[kb] = f32x16{};
-#pragma unroll
-    for (int kk = 0; kk < NQ; ++kk) {
-#pragma unroll
-      for (int kb = 0; kb < kBN / 32; ++kb) {
-        const int off = addr(32 * kb, 32 * kk) - addr(0, 0);
-        bf16x8 a = *(const __attribute__((address_space(3))) bf16x8*)(kt + kbase + off);
-        s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, f.v[kk], s[kb], 0, 0, 0);
-      }
-    }
-  }
-
-  // The same product with the accumulators in VGPRs (for kernels run at one wave per
-  // SIMD, whose MFMAs the compiler would otherwise give AGPR results).  The caller
-  // must leave the XDL-to-VALU wait states (xdl_result_guard) before reading s.
+  // S^T (two 32-key blocks) = K_tile Q^T, with the accumulators in VGPRs: at one wave
+  // per SIMD the compiler would give the MFMAs AGPR results, which the softmax would
+  // have to copy out.  The caller must leave the XDL-to-VALU wait states
+  // (xdl_result_guard) before reading s.
   __device__ static void scores_vgpr(f32x16 (&s)[kBN / 32], const QFrag& f, const lds_char* kt, int kbase) {
 #pragma unroll
     for (int kk = 0; kk < NQ; ++kk) {
@@ -627,19 +613,17 @@ struct Softmax {
 // DMA and meets the other waves at the one barrier of the iteration.  The last
 // tile, whose keys may be masked, takes its max after the loop.
 //
-// For D >= 128 the iteration is written as fixed slots -- one MFMA, the LDS
-// operand read for the MFMA kRing slots later, a share of the softmax work
-// and, in the first slots, one block of the next tiles' DMA -- separated by
-// sched_barrier fences that keep the compiler from regrouping them.  At
-// D = 256 (one wave per SIMD) nothing else hides a stall; at D = 128 (two
-// waves per SIMD) the fixed order still measured 4% faster than the
-// compiler's.  D = 64 keeps the compiler's order.
+// The iteration is written as fixed slots -- one MFMA, the LDS operand read
+// for the MFMA kRing slots later, a share of the softmax work and, in the
+// first slots, one block of the next tiles' DMA -- separated by sched_barrier
+// fences that keep the compiler from regrouping them.  At D = 256 (one wave
+// per SIMD) nothing else hides a stall; at D = 128 and 64 (two waves per SIMD)
+// the fixed order still measured 4-4.5% faster than the compiler's.
 constexpr int kRing = 2;  // LDS operand reads issued this many slots ahead (2..4 measure the same)
 
 template <int D, bool PARTIAL, bool STREAM>
 __device__ __forceinline__ void bf16_fwd_dma(const FwdArgs& a, char* smem_generic) {
   using P = Bf16Dma<D>;
-  constexpr bool kManual = (D >= 128);
   lds_char* const smem = (lds_char*)smem_generic;
   lds_char* const kbuf0 = smem;
   lds_char* const kbuf1 = smem + P::TILE_BYTES;
@@ -688,19 +672,16 @@ __device__ __forceinline__ void bf16_fwd_dma(const FwdArgs& a, char* smem_generi
   __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's tile loads have landed in LDS
   __syncthreads();
   f32x16 s_cur[kBN / 32];
-  if constexpr (kManual) {  // same register form as the loop's score MFMAs
+  // S_0, with the loop's register form of the score MFMAs
 #pragma unroll
-    for (int kk = 0; kk < P::NQ; ++kk)
+  for (int kk = 0; kk < P::NQ; ++kk)
 #pragma unroll
-      for (int kb = 0; kb < kBN / 32; ++kb) {
-        const bf16x8 kf = P::k_frag(kbuf0, kbase, (kBN / 32) * kk + kb);
-        if (kk == 0) mfma_vgpr_first(s_cur[kb], kf, qf.v[0]);
-        else mfma_vgpr_acc(s_cur[kb], kf, qf.v[kk]);
-      }
-    asm volatile("s_nop 7\n\ts_nop 7" ::: "memory");  // XDL result -> VALU read (row_max below)
-  } else {
-    P::scores(s_cur, qf, kbuf0, kbase);
-  }
+    for (int kb = 0; kb < kBN / 32; ++kb) {
+      const bf16x8 kf = P::k_frag(kbuf0, kbase, (kBN / 32) * kk + kb);
+      if (kk == 0) mfma_vgpr_first(s_cur[kb], kf, qf.v[0]);
+      else mfma_vgpr_acc(s_cur[kb], kf, qf.v[kk]);
+    }
+  asm volatile("s_nop 7\n\ts_nop 7" ::: "memory");  // XDL result -> VALU read (row_max below)
   __syncthreads();  // every wave is done with K_0 before its buffer is refilled
 
   f32x16 o[D / 32];
@@ -719,15 +700,7 @@ __device__ __forceinline__ void bf16_fwd_dma(const FwdArgs& a, char* smem_generi
     lds_char* const v_cur = (j & 1) ? vbuf1 : vbuf0;   // V_j
     lds_char* const v_free = (j & 1) ? vbuf0 : vbuf1;  // V_{j-1} consumed -> V_{j+1}
     const __amdgpu_buffer_rsrc_t k_rs = k_tile(j + 2), v_rs = v_tile(j + 1);
-    if constexpr (!kManual) {
-      P::template dma_tile<STREAM>(k_rs, k_free, wave_u, lane);
-      P::template dma_tile<STREAM>(v_rs, v_free, wave_u, lane);
-    }
-    if constexpr (!kManual) {
-#pragma unroll
-      for (int kb = 0; kb < kBN / 32; ++kb) sn[kb] = f32x16{};
-    }
-    if constexpr (kManual) {
+    {
       constexpr int R = kRing;
       constexpr int NS = P::NQ * (kBN / 32);     // QK^T MFMAs per tile
       constexpr int NV = (D / 32) * (kBN / 16);  // PV MFMAs per tile
@@ -793,18 +766,13 @@ __device__ __forceinline__ void bf16_fwd_dma(const FwdArgs& a, char* smem_generi
         __builtin_amdgcn_sched_barrier(0);
       }
       if constexpr (NEXT_MAX) sm.apply_max(pair_max(mx) * c, o);
-    } else {
-      P::scores(sn, qf, k_next, kbase);
-      sm.template exp_pack<false>(sc, c, pk, kBN, h_half);
-      P::accumulate(o, pk, v_cur, vbase);
-      if constexpr (NEXT_MAX) sm.apply_max(Softmax<D>::row_max(sn, c), o);
     }
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this iteration's tile loads have landed
     lds_barrier();
   };
 
   f32x16 s_alt[kBN / 32];
-  if constexpr (kManual) {
+  {  // unrolled by two so that the score register sets alternate without copies
     int j = 0;
     for (; j + 1 < T - 2; j += 2) {
       iteration(j, std::true_type{}, s_cur, s_alt);
@@ -814,17 +782,6 @@ __device__ __forceinline__ void bf16_fwd_dma(const FwdArgs& a, char* smem_generi
       iteration(j, std::true_type{}, s_cur, s_alt);
       iteration(j + 1, std::false_type{}, s_alt, s_cur);
     } else if (T >= 2) {
-      iteration(T - 2, std::false_type{}, s_cur, s_alt);
-#pragma unroll
-      for (int kb = 0; kb < kBN / 32; ++kb) s_cur[kb] = s_alt[kb];
-    }
-  } else {
-    for (int j = 0; j < T - 2; ++j) {
-      iteration(j, std::true_type{}, s_cur, s_alt);
-#pragma unroll
-      for (int kb = 0; kb < kBN / 32; ++kb) s_cur[kb] = s_alt[kb];
-    }
-    if (T >= 2) {  // the last tile may be masked: its max is taken after the loop
       iteration(T - 2, std::false_type{}, s_cur, s_alt);
 #pragma unroll
       for (int kb = 0; kb < kBN / 32; ++kb) s_cur[kb] = s_alt[kb];
