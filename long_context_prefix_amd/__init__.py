@@ -36,4 +36,4 @@ from ._lib import (  # noqa: F401
     status_string,
 )
 
-__version__ = "0.1.0"
+__version__ = "0.2.0"

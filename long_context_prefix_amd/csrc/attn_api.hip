@@ -123,7 +123,7 @@ attn_status_t launch_bwd(const BwdArgs& base, int64_t rows, int64_t grid_dq, int
 
 extern "C" {
 
-int attn_version(void) { return (0 << 16) | (1 << 8) | 0; }
+int attn_version(void) { return (0 << 16) | (2 << 8) | 0; }
 
 attn_status_t attn_prefix_mask_to_kv_len(const uint8_t* mask, int B, int S, int64_t row_stride, int32_t* kv_len,
                                          void* stream) {

@@ -51,7 +51,7 @@ def test_every_declared_symbol_is_exported(L):
 
 
 def test_version_and_chunks(L):
-    assert L.attn_version() == (0 << 16) | (1 << 8)
+    assert L.attn_version() == (0 << 16) | (2 << 8)
     assert L.attn_splitkv_num_chunks(102400, 4096) == 25
     assert L.attn_splitkv_num_chunks(4096, 4096) == 1
     assert L.attn_splitkv_num_chunks(4097, 4096) == 2
