@@ -816,23 +816,35 @@ __device__ __forceinline__ void bf16_fwd_dma(const FwdArgs& a, char* smem_generi
 template <int D, bool OUT_F32>
 __device__ __forceinline__ void merge_row4(const float* pl, const float* po, int C, int Tq, void* out, float* lse,
                                            int64_t row, int col) {
+  // eight chunks' loads in flight at a time; the sums still run in chunk order
+  constexpr int U = 8;
   float mx = -__builtin_inff();
-  for (int c = 0; c < C; ++c) mx = fmaxf(mx, pl[(int64_t)c * Tq]);
+  {
+    int c = 0;
+    for (; c + U <= C; c += U) {
+      float lc[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) lc[u] = pl[(int64_t)(c + u) * Tq];
+#pragma unroll
+      for (int u = 0; u < U; ++u) mx = fmaxf(mx, lc[u]);
+    }
+    for (; c < C; ++c) mx = fmaxf(mx, pl[(int64_t)c * Tq]);
+  }
 
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
   float wsum = 0.f;
   if (mx != -__builtin_inff()) {
     int c = 0;
-    for (; c + 4 <= C; c += 4) {
-      f32x4 x[4];
-      float lc[4];
+    for (; c + U <= C; c += U) {
+      f32x4 x[U];
+      float lc[U];
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
+      for (int u = 0; u < U; ++u) {
         lc[u] = pl[(int64_t)(c + u) * Tq];
         x[u] = *reinterpret_cast<const f32x4*>(po + (int64_t)(c + u) * Tq * D);
       }
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
+      for (int u = 0; u < U; ++u) {
         const float w = __builtin_amdgcn_exp2f((lc[u] - mx) * kLog2e);
         wsum += w;
         acc += w * x[u];
