@@ -89,3 +89,24 @@ def test_backward_ragged_32k():
                                to64(dout[sl]))
     assert_grad_parity("dk (one head)", dk[sl][:, :, :n], rk, w.name)
     assert_grad_parity("dv (one head)", dv[sl][:, :, :n], rv, w.name)
+
+
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("name", ["icl_121k", "ragged_32k"])
+def test_full_size_determinism_and_padding_invariance(name):
+    """At full size: two runs give the same bits, and NaN in every padded key slot changes no bit."""
+    w = WORKLOADS[name]
+    lens = w.lens()
+    log(f"workload {name}: determinism and NaN-pad invariance, kv_len={lens.tolist()}")
+    q, k, v, kv = make_workload(w, device=DEV)
+    out, lse = _lib.attn_prefix_fwd(q, k, v, kv, w.scale)
+    out2, lse2 = _lib.attn_prefix_fwd(q, k, v, kv, w.scale)
+    torch.cuda.synchronize()
+    assert torch.equal(out, out2) and torch.equal(lse, lse2), "two runs differ"
+    del out2, lse2
+    for b, n in enumerate(lens):
+        k[b, :, int(n):] = float("nan")
+        v[b, :, int(n):] = float("nan")
+    out3, lse3 = _lib.attn_prefix_fwd(q, k, v, kv, w.scale)
+    torch.cuda.synchronize()
+    assert torch.equal(out, out3) and torch.equal(lse, lse3), "padded slots changed the result"
