@@ -107,6 +107,7 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--no-splitkv", action="store_true", help="skip the split-KV workload")
     ap.add_argument("--no-backward", action="store_true", help="skip the backward workload")
+    ap.add_argument("--no-icl16k", action="store_true", help="skip the warm / MALL-scrubbed 16k ICL leg")
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle timing and parity sample")
     ap.add_argument("--cpu-rows", type=int, default=4096, help="oracle query rows per head for the CPU baseline")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -283,6 +284,51 @@ def main() -> int:
             },
         }
         del q, k, v, po, pl, out, lse
+        torch.cuda.empty_cache()
+
+    # ------------------------------------------------- 16k ICL, warm and cold
+    # Its 134 MB of K/V fits the 256 MB MALL: time it with the cache warm, and after a
+    # 1 GiB write that evicts it (the event pair brackets the kernel only).
+    if not args.no_icl16k:
+        wi = WORKLOADS["icl_16k"]
+        log(f"generating {wi.name}: B={wi.B} H={wi.H} D={wi.D} Tq={wi.Tq} S={wi.S}")
+        q, k, v, kv = make_workload(wi, device="cuda")
+        out = torch.empty_like(q)
+        lse = torch.empty((wi.B, wi.H, wi.Tq), dtype=torch.float32, device="cuda")
+        scrub = torch.empty(1 << 28, dtype=torch.float32, device="cuda")
+        fl16 = 4.0 * wi.D * wi.H * wi.Tq * float(wi.lens().sum())
+
+        def icl16():
+            _lib.attn_prefix_fwd(q, k, v, kv, wi.scale, out=out, lse=lse)
+
+        icl16()
+        torch.cuda.synchronize()
+        reps = max(5, args.steps)
+        warm, cold = [], []
+        for _ in range(reps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            icl16()
+            e1.record()
+            torch.cuda.synchronize()
+            warm.append(e0.elapsed_time(e1))
+        for _ in range(reps):
+            scrub.fill_(1.0)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            icl16()
+            e1.record()
+            torch.cuda.synchronize()
+            cold.append(e0.elapsed_time(e1))
+        mw, mc = sorted(warm)[len(warm) // 2], sorted(cold)[len(cold) // 2]
+        log(f"icl_16k: warm {mw:.3f} ms, after a 1 GiB scrub {mc:.3f} ms")
+        result["icl_16k"] = {
+            "workload": wi.name, "B": wi.B, "H": wi.H, "head_dim": wi.D, "T_q": wi.Tq, "S": wi.S,
+            "warm_ms_median": round(mw, 4), "scrubbed_ms_median": round(mc, 4),
+            "warm_tflops": round(fl16 / (mw * 1e-3) / 1e12, 2), "scrubbed_tflops": round(fl16 / (mc * 1e-3) / 1e12, 2),
+            "pct_mfma_peak_warm": round(100 * fl16 / (mw * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 2),
+        }
+        del q, k, v, out, lse, scrub
         torch.cuda.empty_cache()
 
     # ------------------------------------------------------------- backward
