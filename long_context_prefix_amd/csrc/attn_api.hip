@@ -5,6 +5,7 @@
 #include <math.h>
 #include <stdio.h>
 #include <stdlib.h>
+#include <string.h>
 
 #include "attn_bwd_kernels.hpp"
 #include "attn_kernels.hpp"
@@ -94,6 +95,53 @@ attn_status_t dispatch_fwd(const FwdArgs& a, int D, attn_dtype_t dtype, int64_t 
     }
   }
   return ATTN_ERR_UNSUPPORTED;
+}
+
+// D = 256, bf16, more than kBM query rows per head: 64 rows per wave, 256 per workgroup.
+template <bool PARTIAL>
+attn_status_t launch_fwd_wide(FwdArgs a, int B, int H, hipStream_t stream, const char* tag) {
+  a.n_qtiles = (a.Tq + kBMW - 1) / kBMW;
+  const int64_t grid = (int64_t)a.n_qtiles * B * H * (PARTIAL ? a.C : 1);
+  const bool stream_kv = a.n_qtiles == 1;
+  if (verbose())
+    fprintf(stderr, "[attn_prefix] %s D=256 bf16 wide grid=%lld block=%d lds=%d%s\n", tag, (long long)grid, kThreads,
+            WideLayout::LDS_BYTES, stream_kv ? " streaming" : "");
+  (void)hipGetLastError();
+  if (stream_kv)
+    hipLaunchKernelGGL((attn_fwd_wide_kernel<PARTIAL, true>), dim3((unsigned)grid), dim3(kThreads), 0, stream, a);
+  else
+    hipLaunchKernelGGL((attn_fwd_wide_kernel<PARTIAL, false>), dim3((unsigned)grid), dim3(kThreads), 0, stream, a);
+  return hipGetLastError() == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
+}
+
+// Compute units of the current device (cached per device; 256 if the query fails).
+int device_cus() {
+  static int cached[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cached[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    cached[dev] = n;
+  }
+  return cached[dev];
+}
+
+// Which D = 256 bf16 forward kernel a launch takes.  The 64-row kernel does about 8% more
+// work per unit time than the 32-row one, but its workgroups are twice as large, so the
+// last wave of workgroups is emptier: it is taken when its waves, each worth 2 / 1.08 of a
+// 32-row wave, come to fewer.  ATTN_PREFIX_FWD_ROWS=128 or 256 forces either kernel.
+bool use_wide(int D, attn_dtype_t dtype, int B, int H, int Tq) {
+  if (dtype != ATTN_BF16 || D != 256) return false;
+  const char* e = getenv("ATTN_PREFIX_FWD_ROWS");
+  if (e && strcmp(e, "256") == 0) return true;
+  if (e && strcmp(e, "128") == 0) return false;
+  if (Tq <= kBM) return false;
+  const int64_t cus = device_cus();
+  const int64_t heads = (int64_t)B * H;
+  const int64_t waves_narrow = (heads * ((Tq + kBM - 1) / kBM) + cus - 1) / cus;
+  const int64_t waves_wide = (heads * ((Tq + kBMW - 1) / kBMW) + cus - 1) / cus;
+  return waves_wide * 200 < waves_narrow * 108;
 }
 
 // WPE_DKDV = 0 selects the cross-tile pipelined dk/dv kernel (one wave per SIMD), otherwise
@@ -230,6 +278,7 @@ attn_status_t attn_prefix_fwd(const void* q, const void* k, const void* v, const
   a.n_qtiles = (Tq + kBM - 1) / kBM;
   a.out = out;
   a.lse = lse;
+  if (use_wide(D, dtype, B, H, Tq)) return launch_fwd_wide<false>(a, B, H, reinterpret_cast<hipStream_t>(stream), "prefix_fwd");
   const int64_t grid = (int64_t)a.n_qtiles * B * H;
   return dispatch_fwd<false>(a, D, dtype, grid, reinterpret_cast<hipStream_t>(stream));
 }

@@ -37,6 +37,7 @@
 namespace lcp {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
@@ -82,7 +83,6 @@ __device__ __forceinline__ int st_key(int kb, int r, int h) { return 32 * kb + 8
 
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   // round to nearest even (v_cvt_pk_bf16_f32)
-  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
   bf16x2 p = {(__bf16)lo, (__bf16)hi};
   return __builtin_bit_cast(uint32_t, p);
 }
@@ -111,6 +111,14 @@ __device__ __forceinline__ void mfma_vgpr_first(f32x16& d, bf16x8 a, bf16x8 b) {
 }
 __device__ __forceinline__ void mfma_vgpr_acc(f32x16& d, bf16x8 a, bf16x8 b) {
   asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(d) : "v"(a), "v"(b));
+}
+
+// O^T accumulation for the kernel whose register file is full (64 rows per wave at
+// D = 256): the accumulator is kept in AGPRs and the operands in VGPRs by the constraints,
+// so the compiler cannot move O between register files around the MFMA.  Any VALU read
+// of o (v_accvgpr_read) must leave the XDL wait states.
+__device__ __forceinline__ void mfma_agpr_acc(f32x16& o, bf16x8 a, u32x4 b) {
+  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(o) : "v"(a), "v"(b));
 }
 
 // 24 wait states between the last of those MFMAs and any VALU read of their
@@ -146,7 +154,7 @@ struct Bf16Dma {
   static constexpr int NBLK = kBN / RPB;   // blocks per tile (32, 16, 8)
   static constexpr int BLK = 1040;         // padded block stride
   static constexpr int TILE_BYTES = NBLK * BLK;
-  static constexpr int LDS_BYTES = 4 * TILE_BYTES;  // K and V, two buffers each
+  static constexpr int LDS_BYTES = 4 * TILE_BYTES + 16;  // K and V, two buffers each; 4 flags
   static constexpr int NQ = D / 16;
   static constexpr int LPR = ROWB / 16;    // DMA lanes per row
   static constexpr bool kIsF32 = false;
@@ -170,7 +178,7 @@ struct Bf16Dma {
   __host__ __device__ static constexpr int addr(int j, int col) { return blk_of(j) * BLK + row_of(j) * ROWB + col; }
   // the key stored in row r of block b (inverse of blk_of / row_of)
   __host__ __device__ static constexpr int key_of(int b, int r) {
-    int kb, s, g, h, e;
+    int kb = 0, s = 0, g = 0, h = 0, e = 0;
     h = b & 1;
     g = (b >> 1) & 1;
     if constexpr (D == 256) {
@@ -395,8 +403,9 @@ struct Work {
   int64_t bh, out_row;
 };
 
+// local_row: this lane's row within a query tile of tile_rows rows
 template <bool PARTIAL>
-__device__ __forceinline__ Work decode(const FwdArgs& a, int lane, int wave) {
+__device__ __forceinline__ Work decode(const FwdArgs& a, int tile_rows, int local_row) {
   Work w;
   int wg = blockIdx.x;
   const int qt = wg % a.n_qtiles;
@@ -417,7 +426,7 @@ __device__ __forceinline__ Work decode(const FwdArgs& a, int lane, int wave) {
     w.hi = min(w.lo + a.chunk, n);
   }
   w.bh = (int64_t)w.b * a.H + w.h;
-  w.row = qt * kBM + wave * 32 + (lane & 31);
+  w.row = qt * tile_rows + local_row;
   w.row_ok = w.row < a.Tq;
   w.out_row = PARTIAL ? ((w.bh * a.C + w.c) * a.Tq + w.row) : (w.bh * a.Tq + w.row);
   return w;
@@ -463,7 +472,7 @@ __device__ __forceinline__ void attn_fwd_body(const FwdArgs& a, char* smem) {
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int h_half = lane >> 5;
-  const Work w = decode<PARTIAL>(a, lane, wave);
+  const Work w = decode<PARTIAL>(a, kBM, wave * 32 + (lane & 31));
   if (w.hi <= w.lo) {
     write_empty<P, D, PARTIAL>(a, w, h_half);
     return;
@@ -634,7 +643,7 @@ __device__ __forceinline__ void bf16_fwd_dma(const FwdArgs& a, char* smem_generi
   const int lane = tid & 63, wave = tid >> 6;
   const int wave_u = __builtin_amdgcn_readfirstlane(wave);
   const int h_half = lane >> 5;
-  const Work w = decode<PARTIAL>(a, lane, wave);
+  const Work w = decode<PARTIAL>(a, kBM, wave * 32 + (lane & 31));
   if (w.hi <= w.lo) {
     write_empty<P, D, PARTIAL>(a, w, h_half);
     return;
@@ -806,6 +815,350 @@ __device__ __forceinline__ void bf16_fwd_dma(const FwdArgs& a, char* smem_generi
   write_rows<P, D, PARTIAL>(a, w, o, 1.0f / l, (sm.m + __builtin_amdgcn_logf(l)) * kLn2, h_half);
 }
 
+// ------------------------------------------------ bf16, D = 256, 64 rows per wave
+// The same contractions with each wave holding two 32-row groups of queries
+// (64 rows, 256 per workgroup) over 32-key tiles.  Every K operand read and
+// every transposed V read then feeds two MFMAs (one per group), so the LDS
+// operand traffic and the tile DMA per MFMA are half those of bf16_fwd_dma,
+// whose D = 256 form is bound by LDS bandwidth rather than by the MFMA pipe.
+// The register file holds it only just: O of both groups takes all 256 AGPRs,
+// Q of both groups 128 VGPRs.  A 32-key tile is the first 16 blocks of the
+// 64-key layout of Bf16Dma<256> (keys 0..31), so the operand reads and the
+// DMA are those of that layout.  Used for launches with more than kBM query
+// rows per head; short query blocks keep the 32-row kernel, which wastes no
+// rows on a partly filled 256-row tile.
+constexpr int kBMW = 256;  // query rows per workgroup (64 per wave)
+constexpr int kBNW = 32;   // keys per tile
+
+struct WideLayout {
+  using P = Bf16Dma<256>;
+  static constexpr int TILE_BYTES = 16 * P::BLK;
+  static constexpr int LDS_BYTES = 4 * TILE_BYTES;  // K and V, two buffers each
+  static constexpr int DMA_PER_WAVE = 4;            // 16 blocks per tile over 4 waves
+  static_assert(P::key_of(15, 1) < kBNW && P::blk_of(kBNW - 1) < 16, "keys 0..31 fill blocks 0..15");
+
+  // Block b = wave + 4 bi of a tile, as Bf16Dma<256>::dma_block.  The lane's part of the
+  // global offset (row r = lane / 32, chunk lane % 32) is one VGPR for every block; the
+  // block's part, 512 key_of(b, 0), is added into a temporary inside the asm so that no
+  // per-block offset stays live, and so that the whole offset is the VGPR offset that the
+  // buffer range check sees.
+  template <bool STREAM>
+  __device__ static void dma_block(__amdgpu_buffer_rsrc_t rs, lds_char* buf, int wave_u, uint32_t voff, int bi) {
+    const int b = wave_u + 4 * bi;
+    const uint32_t lds = (uint32_t)(uintptr_t)(buf + b * P::BLK);
+    const uint32_t boff = (uint32_t)(P::key_of(b, 0) * P::ROWB);
+    uint32_t t;
+    if constexpr (STREAM)
+      asm volatile(
+          "v_add_u32 %0, %2, %1\n\ts_mov_b32 m0, %3\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %4, 0 offen nt lds"
+          : "=&v"(t)
+          : "v"(voff), "s"(boff), "s"(lds), "s"(rs)
+          : "m0");
+    else
+      asm volatile(
+          "v_add_u32 %0, %2, %1\n\ts_mov_b32 m0, %3\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %4, 0 offen lds"
+          : "=&v"(t)
+          : "v"(voff), "s"(boff), "s"(lds), "s"(rs)
+          : "m0");
+  }
+};
+
+// Rows of group 1 sit 32 below those of group 0.
+__device__ __forceinline__ Work next_group(const FwdArgs& a, Work w) {
+  w.row += 32;
+  w.out_row += 32;
+  w.row_ok = w.row < a.Tq;
+  return w;
+}
+
+// Scaled row max of one 32-key score block (this lane's keys, then its partner lane's).
+__device__ __forceinline__ float row_max32(const f32x16& s, float c) {
+  float mt = fmaxf(s[0], s[1]);
+#pragma unroll
+  for (int r = 2; r < 16; ++r) mt = fmaxf(mt, s[r]);
+  return pair_max(mt) * c;
+}
+
+// XDL wait states before a VALU read of an O tile written by inline MFMAs: the tile is an
+// operand of the asm, so no read of it -- the compiler's own register copies included --
+// can be placed before the wait.
+__device__ __forceinline__ void o_result_guard(f32x16& o) {
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+a"(o));
+}
+// The same for the two score blocks before their first VALU read.
+__device__ __forceinline__ void s_result_guard(f32x16 (&s)[2]) {
+  __builtin_amdgcn_sched_barrier(0);
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+v"(s[0]), "+v"(s[1]));
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+// Softmax state of one lane of the 64-row kernel: its two rows (groups 0 and 1).
+//
+// O is never rescaled inside the tile loop: with O in all 256 AGPRs, an in-place rescale
+// (rare as it is) would make the register allocator hold a second copy of an O tile,
+// which does not fit, and it would spill O in the hot loop.  Instead all probabilities of
+// a pass are taken against one reference per row: the first tile's (scaled) max.  No
+// per-tile max is taken: a tile is checked through its sums instead.  While a lane's sum
+// over a tile stays at or below 2^kWideSlackLog2, every p of it does too, so the tile's
+// scores are at most the reference + kWideSlackLog2 and the sums cannot overflow (for
+// finite V below 2^90).  A tile that breaks this marks the pass bad and records its exact
+// max; the workgroup then runs the pass again against max(reference + kWideSlackLog2,
+// recorded maxima), which every score of the row is at or below.  O / l is the same
+// softmax either way: only the common scale differs.
+constexpr float kWideSlackLog2 = 20.0f;
+
+struct WideSoftmax {
+  float m[2];     // the reference this pass takes probabilities against
+  float mtop[2];  // the largest exact max of a tile that broke the slack (or -inf)
+  float l[2] = {0.f, 0.f};
+  bool bad = false;  // some tile of this wave broke the slack in this pass
+};
+
+template <bool PARTIAL, bool STREAM>
+__device__ __forceinline__ void bf16_fwd_wide(const FwdArgs& a, char* smem_generic) {
+  constexpr int D = 256;
+  using P = Bf16Dma<256>;
+  using L = WideLayout;
+  lds_char* const smem = (lds_char*)smem_generic;
+  lds_char* const kbuf0 = smem;
+  lds_char* const kbuf1 = smem + L::TILE_BYTES;
+  lds_char* const vbuf0 = smem + 2 * L::TILE_BYTES;
+  lds_char* const vbuf1 = smem + 3 * L::TILE_BYTES;
+  volatile __attribute__((address_space(3))) int* const bad_flag =
+      (volatile __attribute__((address_space(3))) int*)(smem + 4 * L::TILE_BYTES);  // one per wave
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+  const int h_half = lane >> 5;
+  Work w[2];
+  w[0] = decode<PARTIAL>(a, kBMW, wave * 64 + (lane & 31));
+  w[1] = next_group(a, w[0]);
+  if (w[0].hi <= w[0].lo) {
+    write_empty<P, D, PARTIAL>(a, w[0], h_half);
+    write_empty<P, D, PARTIAL>(a, w[1], h_half);
+    return;
+  }
+  const uint32_t dma_voff = (uint32_t)((lane >> 5) * 16 * (D * 2) + (lane & 31) * 16);
+  const int nkeys = w[0].hi - w[0].lo;
+  const int T = (nkeys + kBNW - 1) / kBNW;
+  auto nv_of = [&](int t) {
+    const int r = nkeys - t * kBNW;
+    return r < 0 ? 0 : (r > kBNW ? kBNW : r);
+  };
+  const uint16_t* kg = reinterpret_cast<const uint16_t*>(a.k) + (w[0].bh * a.S + w[0].lo) * D;
+  const uint16_t* vg = reinterpret_cast<const uint16_t*>(a.v) + (w[0].bh * a.S + w[0].lo) * D;
+  auto k_tile = [&](int t) { return make_rsrc(kg + (int64_t)t * kBNW * D, (uint32_t)nv_of(t) * (D * 2)); };
+  auto v_tile = [&](int t) { return make_rsrc(vg + (int64_t)t * kBNW * D, (uint32_t)nv_of(t) * (D * 2)); };
+  auto dma = [&](__amdgpu_buffer_rsrc_t rs, lds_char* buf) {
+#pragma unroll
+    for (int bi = 0; bi < L::DMA_PER_WAVE; ++bi) L::template dma_block<STREAM>(rs, buf, wave_u, dma_voff, bi);
+  };
+
+  typename P::QFrag qf[2];
+#pragma unroll
+  for (int g = 0; g < 2; ++g) {
+    const uint16_t* qrow =
+        reinterpret_cast<const uint16_t*>(a.q) + (w[g].bh * a.Tq + (w[g].row_ok ? w[g].row : 0)) * D;
+    P::load_q(qf[g], qrow, w[g].row_ok, h_half);
+  }
+  float c = a.scale_log2;
+  if (c < 0.0f) {  // c * (q.k) == |c| * ((-q).k): keep c >= 0 so raw-score maxima are the scaled maxima
+    c = -c;
+#pragma unroll
+    for (int g = 0; g < 2; ++g)
+#pragma unroll
+      for (int kk = 0; kk < P::NQ; ++kk) {
+        u32x4 x = __builtin_bit_cast(u32x4, qf[g].v[kk]) ^ 0x80008000u;
+        qf[g].v[kk] = __builtin_bit_cast(bf16x8, x);
+      }
+  }
+  // masked keys are -inf scores, and c * -inf must stay -inf: a zero scale is taken as the
+  // smallest normal float (every finite score then gives 2^0 = 1 to within fp32 rounding)
+  c = fmaxf(c, 1.17549435e-38f);
+  const int kbase = P::k_base(lane);
+  const int vbase = P::v_base(lane);
+
+  f32x16 o[2][D / 32];
+  WideSoftmax sm;
+  sm.m[0] = sm.m[1] = -__builtin_inff();
+  sm.mtop[0] = sm.mtop[1] = -__builtin_inff();
+  f32x16 s[2];     // scores of the tile in flight, one block per group
+  u32x4 pa[2][2];  // P of one tile: group g, keys 16 ks .. 16 ks + 15 (two sets, used alternately)
+  u32x4 pb[2][2];
+
+  // Softmax of the scores in s for a tile with nv valid keys, spread over the 32 slots of a PV
+  // phase: slots 0..7 take the row maxima (four elements each), slot 8 moves m where needed,
+  // slots 8..23 take the exponentials (two elements each, staged as in bf16_fwd_dma: the fma
+  // of element e + 2, the exp2 of e + 1, the sum and bf16 pack of e) into pk.
+  constexpr int R = kRing;
+  // Exponentials of the scores in s into pk, one element per slot (element e: group e / 16,
+  // register e % 16), staged so that no instruction waits on the one just before it: the
+  // fma of element e + 2, the exp2 of e + 1, then the fp32 sum of e and the bf16 pack of
+  // e - 1 and e.
+  auto softmax_slot = [&](int e, u32x4 (&pk)[2][2], float (&xe)[32], float (&pe)[32], float (&acc)[2]) {
+    auto fma_of = [&](int k) { return __builtin_fmaf(s[k >> 4][k & 15], c, -sm.m[k >> 4]); };
+    if (e == 0) {
+      xe[0] = fma_of(0);
+      xe[1] = fma_of(1);
+      pe[0] = __builtin_amdgcn_exp2f(xe[0]);
+    }
+    if (e + 2 < 32) xe[e + 2] = fma_of(e + 2);
+    if (e + 1 < 32) pe[e + 1] = __builtin_amdgcn_exp2f(xe[e + 1]);
+    acc[e >> 4] += pe[e];
+    if (e & 1) pk[e >> 4][(e >> 3) & 1][(e & 7) >> 1] = pack_bf16x2(pe[e - 1], pe[e]);
+  };
+  // After a tile's exponentials: add the sums to l, and if a lane's sum broke the slack,
+  // record the tile's exact scaled max (rare; the scores are still in s) and mark the pass.
+  auto softmax_end = [&](float (&acc)[2]) {
+    const float slack = __builtin_exp2f(kWideSlackLog2);
+    const bool hot = !(acc[0] <= slack) || !(acc[1] <= slack);
+#pragma unroll
+    for (int g = 0; g < 2; ++g) sm.l[g] += acc[g];
+    if (__builtin_amdgcn_ballot_w64(hot) != 0) {
+      sm.bad = true;
+#pragma unroll
+      for (int g = 0; g < 2; ++g) sm.mtop[g] = fmaxf(sm.mtop[g], row_max32(s[g], c));
+    }
+  };
+  // keys at or past nv in the tile of s count as -inf: p = 2^-inf = 0 (c > 0)
+  auto mask_scores = [&](int nv) {
+#pragma unroll
+    for (int g = 0; g < 2; ++g)
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+        if (st_key(0, r, h_half) >= nv) s[g][r] = -__builtin_inff();
+  };
+  // the first tile of a pass, without PV products beside it: its max is the reference of a
+  // first pass
+  auto softmax_first = [&](u32x4 (&pk)[2][2]) {
+#pragma unroll
+    for (int g = 0; g < 2; ++g)
+      if (sm.m[g] == -__builtin_inff()) sm.m[g] = row_max32(s[g], c);
+    float xe[32], pe[32], acc[2] = {0.f, 0.f};
+#pragma unroll
+    for (int e = 0; e < 32; ++e) softmax_slot(e, pk, xe, pe, acc);
+    softmax_end(acc);
+  };
+
+  // S = K_t Q^T for both groups, one K fragment per two MFMAs; kt holds K_t
+  auto qk_first = [&](const lds_char* kt) {
+#pragma unroll
+    for (int kk = 0; kk < P::NQ; ++kk) {
+      const bf16x8 kf = P::k_frag(kt, kbase, 2 * kk);
+#pragma unroll
+      for (int g = 0; g < 2; ++g) {
+        if (kk == 0) mfma_vgpr_first(s[g], kf, qf[g].v[0]);
+        else mfma_vgpr_acc(s[g], kf, qf[g].v[kk]);
+      }
+    }
+  };
+
+
+  // Iteration j: P_j in pc, K_{j+1} and V_j in LDS.  Phase X: 32 QK^T slots (K fragment kk,
+  // group g) computing S_{j+1}, with the DMA of K_{j+2} and V_{j+1} in the first 8.  Phase Y:
+  // 32 PV slots (V fragment, group g) adding V_j P_j to O, with the softmax of S_{j+1} into pn
+  // beside them (S_{j+1} masked first when it is the last tile).  Then the DMA wait and the one
+  // barrier.  One loop body serves every iteration (the buffers are picked at run time and
+  // pn is copied to pc), so that O keeps one register assignment throughout.
+  auto iteration = [&](int j, auto odd_tag, u32x4 (&pc)[2][2], u32x4 (&pn)[2][2]) {
+    constexpr bool odd = decltype(odd_tag)::value;  // j is odd
+    const lds_char* const k_next = odd ? kbuf0 : kbuf1;
+    lds_char* const k_free = odd ? kbuf1 : kbuf0;
+    const lds_char* const v_cur = odd ? vbuf1 : vbuf0;
+    lds_char* const v_free = odd ? vbuf0 : vbuf1;
+    const __amdgpu_buffer_rsrc_t k_rs = k_tile(j + 2), v_rs = v_tile(j + 1);
+    const int nv = nv_of(j + 1);
+    constexpr int NF = P::NQ;  // K fragments (and V fragments) per tile: 16
+    bf16x8 kf[R], vf[R];
+#pragma unroll
+    for (int i = 0; i < R; ++i) kf[i] = P::k_frag(k_next, kbase, 2 * i);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int i = 0; i < 2 * NF; ++i) {
+      const int kk = i >> 1, g = i & 1;
+      if (kk == 0) mfma_vgpr_first(s[g], kf[kk % R], qf[g].v[0]);
+      else mfma_vgpr_acc(s[g], kf[kk % R], qf[g].v[kk]);
+      if (g == 1 && kk + R < NF) kf[kk % R] = P::k_frag(k_next, kbase, 2 * (kk + R));
+      if (i >= 2 * NF - R) vf[i - (2 * NF - R)] = P::v_frag(v_cur, vbase, i - (2 * NF - R));
+      if (i < 2 * L::DMA_PER_WAVE) {
+        if (i < L::DMA_PER_WAVE) L::template dma_block<STREAM>(k_rs, k_free, wave_u, dma_voff, i);
+        else L::template dma_block<STREAM>(v_rs, v_free, wave_u, dma_voff, i - L::DMA_PER_WAVE);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    // the scores were written by MFMAs the compiler does not see as such: keep the VALU
+    // reads of S_{j+1} below clear of the last of them
+    s_result_guard(s);
+    if (nv < kBNW) mask_scores(nv);
+    __builtin_amdgcn_sched_barrier(0);
+    float xe[32], pe[32], acc[2] = {0.f, 0.f};
+#pragma unroll
+    for (int i = 0; i < 2 * NF; ++i) {
+      const int vi = i >> 1, g = i & 1;  // V fragment vi: keys 16 (vi / 8) .., columns 32 (vi % 8) ..
+      mfma_agpr_acc(o[g][vi & 7], vf[vi % R], pc[g][vi >> 3]);
+      if (g == 1 && vi + R < NF) vf[vi % R] = P::v_frag(v_cur, vbase, vi + R);
+      softmax_slot(i, pn, xe, pe, acc);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    softmax_end(acc);
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this iteration's tile loads have landed
+    lds_barrier();
+  };
+  // one pass over the keys; a second runs only if the first marked a row bad (see WideSoftmax)
+  for (int pass = 0;; ++pass) {
+#pragma unroll
+    for (int g = 0; g < 2; ++g)
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db) o[g][db] = f32x16{};
+    sm.l[0] = sm.l[1] = 0.f;
+    dma(k_tile(0), kbuf0);
+    dma(v_tile(0), vbuf0);
+    dma(k_tile(1), kbuf1);
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's tile loads have landed in LDS
+    __syncthreads();
+    qk_first(kbuf0);
+    s_result_guard(s);  // XDL result -> VALU read (row max below)
+    __syncthreads();     // every wave is done with K_0 before its buffer is refilled
+    if (nv_of(0) < kBNW) mask_scores(nv_of(0));
+    softmax_first(pa);
+    // iterations 0 .. T2 - 1 with T2 = T rounded up to even: iteration j adds PV_j and takes
+    // the scores of tile j + 1, so the last one or two iterations take phantom tiles at or past
+    // T, whose keys are all masked (p = 0; their DMA zero-fills LDS without reading memory).
+    // The PV product of tile T - 1 then needs no code of its own, and the loop body is one
+    // pair of iterations, whose P register sets alternate without copies.
+    const int T2 = (T + 1) & ~1;
+    for (int j = 0; j < T2; j += 2) {
+      iteration(j, std::false_type{}, pa, pb);
+      iteration(j + 1, std::true_type{}, pb, pa);
+    }
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // no tile load may still be writing LDS when the pass ends
+    // does any wave of the workgroup need the second pass?
+    if (lane == 0) bad_flag[wave] = sm.bad ? 1 : 0;
+    __syncthreads();
+    const bool redo = (bad_flag[0] | bad_flag[1] | bad_flag[2] | bad_flag[3]) != 0;
+    __syncthreads();  // the flags are read before any wave can write them again
+    if (!redo || pass > 0) break;
+#pragma unroll
+    for (int g = 0; g < 2; ++g) sm.m[g] = fmaxf(sm.m[g] + kWideSlackLog2, sm.mtop[g]);
+    sm.bad = false;
+  }
+
+  // the output rows are recomputed here rather than kept in registers through the loop
+  int tid_e = threadIdx.x;
+  asm volatile("" : "+v"(tid_e));
+  Work we[2];
+  we[0] = decode<PARTIAL>(a, kBMW, (tid_e >> 6) * 64 + (tid_e & 31));
+  we[1] = next_group(a, we[0]);
+#pragma unroll
+  for (int g = 0; g < 2; ++g) {
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db) o_result_guard(o[g][db]);  // the epilogue reads O
+    const float l = pair_sum(sm.l[g]);
+    write_rows<P, D, PARTIAL>(a, we[g], o[g], 1.0f / l, (sm.m[g] + __builtin_amdgcn_logf(l)) * kLn2, (tid_e >> 5) & 1);
+  }
+}
+
 // ------------------------------------------------------------ LSE combine
 // Merge of the C partials of one output row, four columns per thread: with
 // M = max_c L_c, w_c = 2^((L_c - M) log2 e), out = sum_c w_c O_c / sum_c w_c and
@@ -928,6 +1281,14 @@ __device__ __forceinline__ void splitkv_merge_tail(const FwdArgs& a) {
     merge_row4<D, OUT_F32>(pl, po, a.C, a.Tq, a.out, a.lse, bh * a.Tq + i, col);
   }
   if (threadIdx.x == 0) a.counters[cidx] = 0;
+}
+
+// 64 query rows per wave at D = 256 (launches with more than kBM rows per head).
+template <bool PARTIAL, bool STREAM>
+__global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads), amdgpu_waves_per_eu(1, 1)))
+void attn_fwd_wide_kernel(FwdArgs a) {
+  __shared__ __attribute__((aligned(16))) char smem[WideLayout::LDS_BYTES];
+  bf16_fwd_wide<PARTIAL, STREAM>(a, smem);
 }
 
 template <class P, int D, bool PARTIAL, int WAVES_PER_EU, bool STREAM, bool MERGE = false>

@@ -37,12 +37,26 @@ def _oracle(q, k, v, kv, scale):
     return ref_prefix_fwd(_np(q), _np(k), _np(v), kv.cpu().numpy(), scale)
 
 
+@pytest.fixture(params=[128, 256])
+def fwd_rows(request, monkeypatch):
+    """Force the bf16 D = 256 forward kernel: 32 query rows per wave (128 per workgroup) or
+    64 (256 per workgroup).  Other head dims have one kernel; their 256 case is skipped."""
+    monkeypatch.setenv("ATTN_PREFIX_FWD_ROWS", str(request.param))
+    return request.param
+
+
+def _skip_dup(D, rows):
+    if D != 256 and rows == 256:
+        pytest.skip("one bf16 forward kernel at this head dim")
+
+
 @pytest.mark.parametrize("D", [64, 128, 256])
 @pytest.mark.parametrize("Tq", [1, 17, 128, 129])
-def test_edge_matrix_bf16(D, Tq):
+def test_edge_matrix_bf16(D, Tq, fwd_rows):
+    _skip_dup(D, fwd_rows)
     S = 200
     lens = [0, 1, 63, 64, 65, S]
-    log(f"edge bf16 D={D} Tq={Tq} S={S} lens={lens}")
+    log(f"edge bf16 D={D} Tq={Tq} S={S} lens={lens} rows={fwd_rows}")
     q, k, v, kv = make_inputs(len(lens), 2, Tq, S, D, lens, "bf16", 1.0, seed=100 + D + Tq, device=DEV)
     scale = 1.0 / math.sqrt(D)
     out, lse = _run_fused(q, k, v, kv, scale)
@@ -51,8 +65,9 @@ def test_edge_matrix_bf16(D, Tq):
 
 
 @pytest.mark.parametrize("D", [64, 128, 256])
-def test_multi_tile_bf16_sharp(D):
+def test_multi_tile_bf16_sharp(D, fwd_rows):
     """Several query and key tiles, ragged tails, peaky attention (q scaled x4)."""
+    _skip_dup(D, fwd_rows)
     B, H, Tq, S = 2, 3, 300, 777
     lens = [700, 777]
     log(f"sharp bf16 D={D}")
@@ -143,8 +158,9 @@ def test_combine_edge_cases():
 
 
 @pytest.mark.parametrize("D", [128, 256])
-def test_padding_invariance_bitwise(D):
+def test_padding_invariance_bitwise(D, fwd_rows):
     """Pads never read: no pads, +-1e4 pads and NaN pads give identical bits."""
+    _skip_dup(D, fwd_rows)
     B, H, Tq, n = 2, 2, 70, 333
     log(f"padding invariance D={D}")
     q, k, v, kv = make_inputs(B, H, Tq, n, D, [n, 129], "bf16", 1.0, seed=500 + D, device=DEV)
@@ -166,7 +182,7 @@ def test_padding_invariance_bitwise(D):
         assert torch.all(po2[:, :, C1:] == 0) and torch.all(torch.isneginf(pl2[:, :, C1:]))
 
 
-def test_determinism_bitwise():
+def test_determinism_bitwise(fwd_rows):
     q, k, v, kv = make_inputs(2, 4, 300, 1000, 256, [1000, 517], "bf16", 0.7, seed=600, device=DEV)
     o1, l1 = _run_fused(q, k, v, kv, 0.0625)
     o2, l2 = _run_fused(q, k, v, kv, 0.0625)
@@ -261,7 +277,7 @@ def test_splitkv_other_head_dims(D):
 
 
 @pytest.mark.parametrize("scale", [-0.0625, 0.0, 0.9])
-def test_scale_sign_and_zero(scale):
+def test_scale_sign_and_zero(scale, fwd_rows):
     """Negative scales (Q is negated internally), scale 0 (uniform weights) and a large scale."""
     D, B, H, Tq, S = 256, 2, 2, 130, 300
     lens = [300, 77]
@@ -346,3 +362,57 @@ def test_splitkv_single_launch(D, Tq, chunk, dtype):
         assert torch.equal(out, rout) and torch.equal(lse, rlse), f"call {rep}: differs from partial + combine"
     ro, rl = ref_prefix_fwd(to64(q), to64(k), to64(v), np.array(lens), scale)
     assert_parity(out, lse, ro, rl, dtype, f"single-launch split D={D}")
+
+
+# ---- the 64-rows-per-wave D = 256 kernel, forced (the library takes it for large launches)
+@pytest.mark.parametrize("Tq", [129, 256, 257, 511])
+def test_wide_edge_matrix(Tq, monkeypatch):
+    """256-row query tiles with ragged tails, 32-key tiles: n in {0, 1, 31, 32, 33, 64, 65, S}."""
+    monkeypatch.setenv("ATTN_PREFIX_FWD_ROWS", "256")
+    D, S = 256, 200
+    lens = [0, 1, 31, 32, 33, 64, 65, S]
+    log(f"wide edge Tq={Tq} lens={lens}")
+    q, k, v, kv = make_inputs(len(lens), 2, Tq, S, D, lens, "bf16", 1.0, seed=1500 + Tq, device=DEV)
+    scale = 1.0 / math.sqrt(D)
+    out, lse = _run_fused(q, k, v, kv, scale)
+    ro, rl = _oracle(q, k, v, kv, scale)
+    assert_parity(out, lse, ro, rl, "bf16", f"wide edge Tq={Tq}")
+
+
+def _first_tile_margin_log2(q, k, n, scale):
+    """Largest (over rows) amount by which a row's max scaled score climbs above its max over
+    the first 32 keys, in log2 units (the second-pass trigger of the 64-row kernel is 16)."""
+    s = torch.einsum("bhtd,bhsd->bhts", q.double().cpu(), k[:, :, :n].double().cpu()) * scale / math.log(2.0)
+    return (s.amax(-1) - s[..., :32].amax(-1)).max().item()
+
+
+def test_wide_growing_scores_take_second_pass(monkeypatch):
+    """Key norms grow along the sequence, so rows climb far past their first tile's max: the
+    workgroups redo their pass against a reference no score of the row exceeds."""
+    monkeypatch.setenv("ATTN_PREFIX_FWD_ROWS", "256")
+    D, B, H, Tq, S = 256, 1, 2, 300, 2048
+    g = torch.Generator(device=DEV).manual_seed(1600)
+    q = torch.randn(B, H, Tq, D, device=DEV, generator=g).abs().to(torch.bfloat16)
+    ramp = torch.linspace(0.0, 6.0, S, device=DEV).view(1, 1, S, 1)
+    k = (torch.rand(B, H, S, D, device=DEV, generator=g) * ramp).to(torch.bfloat16)
+    v = torch.randn(B, H, S, D, device=DEV, generator=g).to(torch.bfloat16)
+    kv = torch.tensor([S], dtype=torch.int32, device=DEV)
+    scale = 1.0 / math.sqrt(D)
+    assert _first_tile_margin_log2(q, k, S, scale) > 64.0
+    out, lse = _run_fused(q, k, v, kv, scale)
+    ro, rl = _oracle(q, k, v, kv, scale)
+    assert_parity(out, lse, ro, rl, "bf16", "wide growing")
+
+
+def test_wide_one_row_takes_second_pass(monkeypatch):
+    """One query row meets one late key far above everything before it; the other rows of
+    its workgroup do not, and every row must come out right after the redo."""
+    monkeypatch.setenv("ATTN_PREFIX_FWD_ROWS", "256")
+    D, B, H, Tq, S = 256, 1, 1, 512, 1000
+    q, k, v, kv = make_inputs(B, H, Tq, S, D, [S], "bf16", 1.0, seed=1700, device=DEV)
+    scale = 1.0 / math.sqrt(D)
+    k[0, 0, 900] = (q[0, 0, 37].float() * 3.0).to(torch.bfloat16)  # row 37 meets key 900
+    assert _first_tile_margin_log2(q[:, :, 37:38], k, S, scale) > 16.0
+    out, lse = _run_fused(q, k, v, kv, scale)
+    ro, rl = _oracle(q, k, v, kv, scale)
+    assert_parity(out, lse, ro, rl, "bf16", "wide one bad row")
