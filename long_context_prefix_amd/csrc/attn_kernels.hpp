@@ -892,6 +892,11 @@ __device__ __forceinline__ void s_result_guard(f32x16 (&s)[2]) {
   __builtin_amdgcn_sched_barrier(0);
 }
 
+// Marks a branch whose body runs rarely (the last tile's mask, the slack check's max): an
+// empty volatile asm cannot be executed speculatively, so the compiler keeps the branch
+// instead of turning its body into selects computed on every iteration.
+__device__ __forceinline__ void rare_path() { asm volatile(""); }
+
 // Softmax state of one lane of the 64-row kernel: its two rows (groups 0 and 1).
 //
 // O is never rescaled inside the tile loop: with O in all 256 AGPRs, an in-place rescale
@@ -991,7 +996,7 @@ __device__ __forceinline__ void bf16_fwd_wide(const FwdArgs& a, char* smem_gener
   // phase: slots 0..7 take the row maxima (four elements each), slot 8 moves m where needed,
   // slots 8..23 take the exponentials (two elements each, staged as in bf16_fwd_dma: the fma
   // of element e + 2, the exp2 of e + 1, the sum and bf16 pack of e) into pk.
-  constexpr int R = kRing;
+  constexpr int R = 4;  // LDS operand reads issued this many fragments ahead (2 and 3 measure 0.5% slower)
   // Exponentials of the scores in s into pk, one element per slot (element e: group e / 16,
   // register e % 16), staged so that no instruction waits on the one just before it: the
   // fma of element e + 2, the exp2 of e + 1, then the fp32 sum of e and the bf16 pack of
@@ -1006,7 +1011,11 @@ __device__ __forceinline__ void bf16_fwd_wide(const FwdArgs& a, char* smem_gener
     if (e + 2 < 32) xe[e + 2] = fma_of(e + 2);
     if (e + 1 < 32) pe[e + 1] = __builtin_amdgcn_exp2f(xe[e + 1]);
     acc[e >> 4] += pe[e];
-    if (e & 1) pk[e >> 4][(e >> 3) & 1][(e & 7) >> 1] = pack_bf16x2(pe[e - 1], pe[e]);
+    if (e & 1) {
+      uint32_t d = pack_bf16x2(pe[e - 1], pe[e]);
+      asm volatile("" : "+v"(d));  // keeps the pack in this slot (it is used only next iteration)
+      pk[e >> 4][(e >> 3) & 1][(e & 7) >> 1] = d;
+    }
   };
   // After a tile's exponentials: add the sums to l, and if a lane's sum broke the slack,
   // record the tile's exact scaled max (rare; the scores are still in s) and mark the pass.
@@ -1016,18 +1025,23 @@ __device__ __forceinline__ void bf16_fwd_wide(const FwdArgs& a, char* smem_gener
 #pragma unroll
     for (int g = 0; g < 2; ++g) sm.l[g] += acc[g];
     if (__builtin_amdgcn_ballot_w64(hot) != 0) {
+      rare_path();
       sm.bad = true;
 #pragma unroll
       for (int g = 0; g < 2; ++g) sm.mtop[g] = fmaxf(sm.mtop[g], row_max32(s[g], c));
     }
   };
-  // keys at or past nv in the tile of s count as -inf: p = 2^-inf = 0 (c > 0)
+  // keys at or past nv in the tile of s count as -inf: p = 2^-inf = 0 (c > 0).  The key
+  // indices come from an opaque copy of the lane's half, so that they are computed here
+  // (rarely) instead of being hoisted out of the tile loop into 16 live registers.
   auto mask_scores = [&](int nv) {
+    int hh = h_half;
+    asm volatile("" : "+v"(hh));
 #pragma unroll
     for (int g = 0; g < 2; ++g)
 #pragma unroll
       for (int r = 0; r < 16; ++r)
-        if (st_key(0, r, h_half) >= nv) s[g][r] = -__builtin_inff();
+        if (st_key(0, r, hh) >= nv) s[g][r] = -__builtin_inff();
   };
   // the first tile of a pass, without PV products beside it: its max is the reference of a
   // first pass
@@ -1090,7 +1104,10 @@ __device__ __forceinline__ void bf16_fwd_wide(const FwdArgs& a, char* smem_gener
     // the scores were written by MFMAs the compiler does not see as such: keep the VALU
     // reads of S_{j+1} below clear of the last of them
     s_result_guard(s);
-    if (nv < kBNW) mask_scores(nv);
+    if (nv < kBNW) {
+      rare_path();
+      mask_scores(nv);
+    }
     __builtin_amdgcn_sched_barrier(0);
     float xe[32], pe[32], acc[2] = {0.f, 0.f};
 #pragma unroll
