@@ -97,7 +97,7 @@ attn_status_t dispatch_fwd(const FwdArgs& a, int D, attn_dtype_t dtype, int64_t 
   return ATTN_ERR_UNSUPPORTED;
 }
 
-// D = 256, bf16, more than kBM query rows per head: 64 rows per wave, 256 per workgroup.
+// D = 256, bf16, 64 query rows per wave (256 per workgroup); use_wide decides when.
 template <bool PARTIAL>
 attn_status_t launch_fwd_wide(FwdArgs a, int B, int H, hipStream_t stream, const char* tag) {
   a.n_qtiles = (a.Tq + kBMW - 1) / kBMW;

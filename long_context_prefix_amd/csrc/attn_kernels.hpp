@@ -824,9 +824,10 @@ __device__ __forceinline__ void bf16_fwd_dma(const FwdArgs& a, char* smem_generi
 // The register file holds it only just: O of both groups takes all 256 AGPRs,
 // Q of both groups 128 VGPRs.  A 32-key tile is the first 16 blocks of the
 // 64-key layout of Bf16Dma<256> (keys 0..31), so the operand reads and the
-// DMA are those of that layout.  Used for launches with more than kBM query
-// rows per head; short query blocks keep the 32-row kernel, which wastes no
-// rows on a partly filled 256-row tile.
+// DMA are those of that layout.  The host takes it for launches whose
+// workgroups fill the GPU's waves better this way (its tiles are twice as
+// tall, so a last, partly filled wave costs more); the rest keep the 32-row
+// kernel.
 constexpr int kBMW = 256;  // query rows per workgroup (64 per wave)
 constexpr int kBNW = 32;   // keys per tile
 
@@ -905,11 +906,11 @@ __device__ __forceinline__ void rare_path() { asm volatile(""); }
 // a pass are taken against one reference per row: the first tile's (scaled) max.  No
 // per-tile max is taken: a tile is checked through its sums instead.  While a lane's sum
 // over a tile stays at or below 2^kWideSlackLog2, every p of it does too, so the tile's
-// scores are at most the reference + kWideSlackLog2 and the sums cannot overflow (for
-// finite V below 2^90).  A tile that breaks this marks the pass bad and records its exact
-// max; the workgroup then runs the pass again against max(reference + kWideSlackLog2,
-// recorded maxima), which every score of the row is at or below.  O / l is the same
-// softmax either way: only the common scale differs.
+// scores are at most the reference + kWideSlackLog2, and the sums cannot overflow (a row
+// has fewer than 2^22 keys, so this holds for any V below 2^86).  A tile that breaks this
+// marks the pass bad and records its exact max; the workgroup then runs the pass again
+// against max(reference + kWideSlackLog2, recorded maxima), which every score of the row
+// is at or below.  O / l is the same softmax either way: only the common scale differs.
 constexpr float kWideSlackLog2 = 20.0f;
 
 struct WideSoftmax {
@@ -1300,7 +1301,7 @@ __device__ __forceinline__ void splitkv_merge_tail(const FwdArgs& a) {
   if (threadIdx.x == 0) a.counters[cidx] = 0;
 }
 
-// 64 query rows per wave at D = 256 (launches with more than kBM rows per head).
+// 64 query rows per wave at D = 256, bf16 (the host picks it by the wave count, see use_wide).
 template <bool PARTIAL, bool STREAM>
 __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads), amdgpu_waves_per_eu(1, 1)))
 void attn_fwd_wide_kernel(FwdArgs a) {
