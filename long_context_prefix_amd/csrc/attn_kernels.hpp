@@ -886,10 +886,10 @@ __device__ __forceinline__ float row_max32(const f32x16& s, float c) {
 __device__ __forceinline__ void o_result_guard(f32x16& o) {
   asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+a"(o));
 }
-// The same for the two score blocks before their first VALU read.
-__device__ __forceinline__ void s_result_guard(f32x16 (&s)[2]) {
+// The same for two score blocks before their first VALU read.
+__device__ __forceinline__ void s_result_guard(f32x16& s0, f32x16& s1) {
   __builtin_amdgcn_sched_barrier(0);
-  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+v"(s[0]), "+v"(s[1]));
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+v"(s0), "+v"(s1));
   __builtin_amdgcn_sched_barrier(0);
 }
 
@@ -989,94 +989,69 @@ __device__ __forceinline__ void bf16_fwd_wide(const FwdArgs& a, char* smem_gener
   WideSoftmax sm;
   sm.m[0] = sm.m[1] = -__builtin_inff();
   sm.mtop[0] = sm.mtop[1] = -__builtin_inff();
-  f32x16 s[2];     // scores of the tile in flight, one block per group
-  u32x4 pa[2][2];  // P of one tile: group g, keys 16 ks .. 16 ks + 15 (two sets, used alternately)
-  u32x4 pb[2][2];
-
-  // Softmax of the scores in s for a tile with nv valid keys, spread over the 32 slots of a PV
-  // phase: slots 0..7 take the row maxima (four elements each), slot 8 moves m where needed,
-  // slots 8..23 take the exponentials (two elements each, staged as in bf16_fwd_dma: the fma
-  // of element e + 2, the exp2 of e + 1, the sum and bf16 pack of e) into pk.
+  // Scores of the tile in flight: group 0 has one register block, group 1 two (s1a, s1b),
+  // used in alternate iterations, so that group 1's exponentials of tile j run beside the
+  // QK^T MFMAs of tile j + 1 while group 0's run beside the PV MFMAs: each phase carries
+  // half of the softmax.
+  f32x16 s0, s1a, s1b;
+  u32x4 p0a[2], p0b[2];  // P of group 0 (keys 16 ks .. in [ks]): two sets, used alternately
+  u32x4 p1[2];           // P of group 1
   constexpr int R = 4;  // LDS operand reads issued this many fragments ahead (2 and 3 measure 0.5% slower)
-  // Exponentials of the scores in s into pk, one element per slot (element e: group e / 16,
-  // register e % 16), staged so that no instruction waits on the one just before it: the
-  // fma of element e + 2, the exp2 of e + 1, then the fp32 sum of e and the bf16 pack of
-  // e - 1 and e.
-  auto softmax_slot = [&](int e, u32x4 (&pk)[2][2], float (&xe)[32], float (&pe)[32], float (&acc)[2]) {
-    auto fma_of = [&](int k) { return __builtin_fmaf(s[k >> 4][k & 15], c, -sm.m[k >> 4]); };
-    if (e == 0) {
+
+  // Exponentials of one score block sg (group g) into pk, one element r per call, staged so
+  // that no instruction waits on the one just before it: the fma of element r + 2, the exp2
+  // of r + 1, then the fp32 sum of r and the bf16 pack of r - 1 and r.
+  auto exp_slot = [&](const f32x16& sg, int g, int r, u32x4 (&pk)[2], float (&xe)[16], float (&pe)[16],
+                      float& acc) {
+    auto fma_of = [&](int k) { return __builtin_fmaf(sg[k], c, -sm.m[g]); };
+    if (r == 0) {
       xe[0] = fma_of(0);
       xe[1] = fma_of(1);
       pe[0] = __builtin_amdgcn_exp2f(xe[0]);
     }
-    if (e + 2 < 32) xe[e + 2] = fma_of(e + 2);
-    if (e + 1 < 32) pe[e + 1] = __builtin_amdgcn_exp2f(xe[e + 1]);
-    acc[e >> 4] += pe[e];
-    if (e & 1) {
-      uint32_t d = pack_bf16x2(pe[e - 1], pe[e]);
-      asm volatile("" : "+v"(d));  // keeps the pack in this slot (it is used only next iteration)
-      pk[e >> 4][(e >> 3) & 1][(e & 7) >> 1] = d;
+    if (r + 2 < 16) xe[r + 2] = fma_of(r + 2);
+    if (r + 1 < 16) pe[r + 1] = __builtin_amdgcn_exp2f(xe[r + 1]);
+    acc += pe[r];
+    if (r & 1) {
+      uint32_t d = pack_bf16x2(pe[r - 1], pe[r]);
+      asm volatile("" : "+v"(d));  // keeps the pack in this slot (it is used only later)
+      pk[r >> 3][(r & 7) >> 1] = d;
     }
   };
-  // After a tile's exponentials: add the sums to l, and if a lane's sum broke the slack,
-  // record the tile's exact scaled max (rare; the scores are still in s) and mark the pass.
-  auto softmax_end = [&](float (&acc)[2]) {
-    const float slack = __builtin_exp2f(kWideSlackLog2);
-    const bool hot = !(acc[0] <= slack) || !(acc[1] <= slack);
-#pragma unroll
-    for (int g = 0; g < 2; ++g) sm.l[g] += acc[g];
-    if (__builtin_amdgcn_ballot_w64(hot) != 0) {
+  // After a block's exponentials: add the sum to l, and if a lane's sum broke the slack,
+  // record the tile's exact scaled max (rare; the scores are still in sg) and mark the pass.
+  auto exp_end = [&](const f32x16& sg, int g, float acc) {
+    sm.l[g] += acc;
+    if (__builtin_amdgcn_ballot_w64(!(acc <= __builtin_exp2f(kWideSlackLog2))) != 0) {
       rare_path();
       sm.bad = true;
-#pragma unroll
-      for (int g = 0; g < 2; ++g) sm.mtop[g] = fmaxf(sm.mtop[g], row_max32(s[g], c));
+      sm.mtop[g] = fmaxf(sm.mtop[g], row_max32(sg, c));
     }
   };
-  // keys at or past nv in the tile of s count as -inf: p = 2^-inf = 0 (c > 0).  The key
-  // indices come from an opaque copy of the lane's half, so that they are computed here
-  // (rarely) instead of being hoisted out of the tile loop into 16 live registers.
-  auto mask_scores = [&](int nv) {
+  // keys at or past nv in a tile count as -inf: p = 2^-inf = 0 (c > 0).  The key indices
+  // come from an opaque copy of the lane's half, so that they are computed here (rarely)
+  // instead of being hoisted out of the tile loop into 16 live registers.
+  auto mask_scores = [&](f32x16& sg0, f32x16& sg1, int nv) {
     int hh = h_half;
     asm volatile("" : "+v"(hh));
 #pragma unroll
-    for (int g = 0; g < 2; ++g)
-#pragma unroll
-      for (int r = 0; r < 16; ++r)
-        if (st_key(0, r, hh) >= nv) s[g][r] = -__builtin_inff();
-  };
-  // the first tile of a pass, without PV products beside it: its max is the reference of a
-  // first pass
-  auto softmax_first = [&](u32x4 (&pk)[2][2]) {
-#pragma unroll
-    for (int g = 0; g < 2; ++g)
-      if (sm.m[g] == -__builtin_inff()) sm.m[g] = row_max32(s[g], c);
-    float xe[32], pe[32], acc[2] = {0.f, 0.f};
-#pragma unroll
-    for (int e = 0; e < 32; ++e) softmax_slot(e, pk, xe, pe, acc);
-    softmax_end(acc);
-  };
-
-  // S = K_t Q^T for both groups, one K fragment per two MFMAs; kt holds K_t
-  auto qk_first = [&](const lds_char* kt) {
-#pragma unroll
-    for (int kk = 0; kk < P::NQ; ++kk) {
-      const bf16x8 kf = P::k_frag(kt, kbase, 2 * kk);
-#pragma unroll
-      for (int g = 0; g < 2; ++g) {
-        if (kk == 0) mfma_vgpr_first(s[g], kf, qf[g].v[0]);
-        else mfma_vgpr_acc(s[g], kf, qf[g].v[kk]);
+    for (int r = 0; r < 16; ++r)
+      if (st_key(0, r, hh) >= nv) {
+        sg0[r] = -__builtin_inff();
+        sg1[r] = -__builtin_inff();
       }
-    }
   };
 
-
-  // Iteration j: P_j in pc, K_{j+1} and V_j in LDS.  Phase X: 32 QK^T slots (K fragment kk,
-  // group g) computing S_{j+1}, with the DMA of K_{j+2} and V_{j+1} in the first 8.  Phase Y:
-  // 32 PV slots (V fragment, group g) adding V_j P_j to O, with the softmax of S_{j+1} into pn
-  // beside them (S_{j+1} masked first when it is the last tile).  Then the DMA wait and the one
-  // barrier.  One loop body serves every iteration (the buffers are picked at run time and
-  // pn is copied to pc), so that O keeps one register assignment throughout.
-  auto iteration = [&](int j, auto odd_tag, u32x4 (&pc)[2][2], u32x4 (&pn)[2][2]) {
+  // Iteration j.  At its top: group 0 of P_j in p0c, group 1 of S_j in s1c, K_{j+1} and V_j
+  // in LDS.
+  //  * Phase X, 32 QK^T slots (K fragment kk, group g): S_{j+1} = K_{j+1} Q^T into s0 and
+  //    s1n, each K fragment feeding both groups; beside the odd slots, group 1 of S_j (s1c)
+  //    goes to P (p1); beside the first even slots, the DMA of K_{j+2} and V_{j+1}.
+  //  * Phase Y, 32 PV slots (V fragment, group): O += V_j P_j, each V fragment feeding both
+  //    groups; beside the odd slots, group 0 of S_{j+1} goes to P (p0n).  S_{j+1} is masked
+  //    first when it holds keys past n.
+  // Then the DMA wait and the one barrier.
+  auto iteration = [&](int j, auto odd_tag, f32x16& s1c, f32x16& s1n, u32x4 (&p0c)[2], u32x4 (&p0n)[2]) {
     constexpr bool odd = decltype(odd_tag)::value;  // j is odd
     const lds_char* const k_next = odd ? kbuf0 : kbuf1;
     lds_char* const k_free = odd ? kbuf1 : kbuf0;
@@ -1089,40 +1064,49 @@ __device__ __forceinline__ void bf16_fwd_wide(const FwdArgs& a, char* smem_gener
 #pragma unroll
     for (int i = 0; i < R; ++i) kf[i] = P::k_frag(k_next, kbase, 2 * i);
     __builtin_amdgcn_sched_barrier(0);
+    {
+      float xe[16], pe[16], acc = 0.f;
 #pragma unroll
-    for (int i = 0; i < 2 * NF; ++i) {
-      const int kk = i >> 1, g = i & 1;
-      if (kk == 0) mfma_vgpr_first(s[g], kf[kk % R], qf[g].v[0]);
-      else mfma_vgpr_acc(s[g], kf[kk % R], qf[g].v[kk]);
-      if (g == 1 && kk + R < NF) kf[kk % R] = P::k_frag(k_next, kbase, 2 * (kk + R));
-      if (i >= 2 * NF - R) vf[i - (2 * NF - R)] = P::v_frag(v_cur, vbase, i - (2 * NF - R));
-      if (i < 2 * L::DMA_PER_WAVE) {
-        if (i < L::DMA_PER_WAVE) L::template dma_block<STREAM>(k_rs, k_free, wave_u, dma_voff, i);
-        else L::template dma_block<STREAM>(v_rs, v_free, wave_u, dma_voff, i - L::DMA_PER_WAVE);
+      for (int i = 0; i < 2 * NF; ++i) {
+        const int kk = i >> 1, g = i & 1;
+        f32x16& sg = g == 0 ? s0 : s1n;
+        if (kk == 0) mfma_vgpr_first(sg, kf[kk % R], qf[g].v[0]);
+        else mfma_vgpr_acc(sg, kf[kk % R], qf[g].v[kk]);
+        if (g == 1 && kk + R < NF) kf[kk % R] = P::k_frag(k_next, kbase, 2 * (kk + R));
+        if (i >= 2 * NF - R) vf[i - (2 * NF - R)] = P::v_frag(v_cur, vbase, i - (2 * NF - R));
+        if (g == 1) exp_slot(s1c, 1, kk, p1, xe, pe, acc);
+        else if (kk < 2 * L::DMA_PER_WAVE) {
+          if (kk < L::DMA_PER_WAVE) L::template dma_block<STREAM>(k_rs, k_free, wave_u, dma_voff, kk);
+          else L::template dma_block<STREAM>(v_rs, v_free, wave_u, dma_voff, kk - L::DMA_PER_WAVE);
+        }
+        __builtin_amdgcn_sched_barrier(0);
       }
-      __builtin_amdgcn_sched_barrier(0);
+      exp_end(s1c, 1, acc);
     }
     // the scores were written by MFMAs the compiler does not see as such: keep the VALU
     // reads of S_{j+1} below clear of the last of them
-    s_result_guard(s);
+    s_result_guard(s0, s1n);
     if (nv < kBNW) {
       rare_path();
-      mask_scores(nv);
+      mask_scores(s0, s1n, nv);
     }
     __builtin_amdgcn_sched_barrier(0);
-    float xe[32], pe[32], acc[2] = {0.f, 0.f};
+    {
+      float xe[16], pe[16], acc = 0.f;
 #pragma unroll
-    for (int i = 0; i < 2 * NF; ++i) {
-      const int vi = i >> 1, g = i & 1;  // V fragment vi: keys 16 (vi / 8) .., columns 32 (vi % 8) ..
-      mfma_agpr_acc(o[g][vi & 7], vf[vi % R], pc[g][vi >> 3]);
-      if (g == 1 && vi + R < NF) vf[vi % R] = P::v_frag(v_cur, vbase, vi + R);
-      softmax_slot(i, pn, xe, pe, acc);
-      __builtin_amdgcn_sched_barrier(0);
+      for (int i = 0; i < 2 * NF; ++i) {
+        const int vi = i >> 1, g = i & 1;  // V fragment vi: keys 16 (vi / 8) .., columns 32 (vi % 8) ..
+        mfma_agpr_acc(o[g][vi & 7], vf[vi % R], g == 0 ? p0c[vi >> 3] : p1[vi >> 3]);
+        if (g == 1 && vi + R < NF) vf[vi % R] = P::v_frag(v_cur, vbase, vi + R);
+        if (g == 1) exp_slot(s0, 0, vi, p0n, xe, pe, acc);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      exp_end(s0, 0, acc);
     }
-    softmax_end(acc);
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this iteration's tile loads have landed
     lds_barrier();
   };
+
   // one pass over the keys; a second runs only if the first marked a row bad (see WideSoftmax)
   for (int pass = 0;; ++pass) {
 #pragma unroll
@@ -1135,20 +1119,42 @@ __device__ __forceinline__ void bf16_fwd_wide(const FwdArgs& a, char* smem_gener
     dma(k_tile(1), kbuf1);
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's tile loads have landed in LDS
     __syncthreads();
-    qk_first(kbuf0);
-    s_result_guard(s);  // XDL result -> VALU read (row max below)
-    __syncthreads();     // every wave is done with K_0 before its buffer is refilled
-    if (nv_of(0) < kBNW) mask_scores(nv_of(0));
-    softmax_first(pa);
+    // S_0 = K_0 Q^T, one K fragment per two MFMAs
+#pragma unroll
+    for (int kk = 0; kk < P::NQ; ++kk) {
+      const bf16x8 kf = P::k_frag(kbuf0, kbase, 2 * kk);
+      if (kk == 0) {
+        mfma_vgpr_first(s0, kf, qf[0].v[0]);
+        mfma_vgpr_first(s1a, kf, qf[1].v[0]);
+      } else {
+        mfma_vgpr_acc(s0, kf, qf[0].v[kk]);
+        mfma_vgpr_acc(s1a, kf, qf[1].v[kk]);
+      }
+    }
+    s_result_guard(s0, s1a);  // XDL result -> VALU read (row max below)
+    __syncthreads();          // every wave is done with K_0 before its buffer is refilled
+    if (nv_of(0) < kBNW) mask_scores(s0, s1a, nv_of(0));
+    // the first tile's max is the reference of a first pass; group 0's exponentials are
+    // taken here, group 1's (still in s1a) in the first iteration
+    if (sm.m[0] == -__builtin_inff()) {
+      sm.m[0] = row_max32(s0, c);
+      sm.m[1] = row_max32(s1a, c);
+    }
+    {
+      float xe[16], pe[16], acc = 0.f;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) exp_slot(s0, 0, r, p0a, xe, pe, acc);
+      exp_end(s0, 0, acc);
+    }
     // iterations 0 .. T2 - 1 with T2 = T rounded up to even: iteration j adds PV_j and takes
     // the scores of tile j + 1, so the last one or two iterations take phantom tiles at or past
     // T, whose keys are all masked (p = 0; their DMA zero-fills LDS without reading memory).
     // The PV product of tile T - 1 then needs no code of its own, and the loop body is one
-    // pair of iterations, whose P register sets alternate without copies.
+    // pair of iterations, whose register sets alternate without copies.
     const int T2 = (T + 1) & ~1;
     for (int j = 0; j < T2; j += 2) {
-      iteration(j, std::false_type{}, pa, pb);
-      iteration(j + 1, std::true_type{}, pb, pa);
+      iteration(j, std::false_type{}, s1a, s1b, p0a, p0b);
+      iteration(j + 1, std::true_type{}, s1b, s1a, p0b, p0a);
     }
     __builtin_amdgcn_s_waitcnt(0x0F70);  // no tile load may still be writing LDS when the pass ends
     // does any wave of the workgroup need the second pass?
