@@ -97,7 +97,7 @@ attn_status_t dispatch_fwd(const FwdArgs& a, int D, attn_dtype_t dtype, int64_t 
   return ATTN_ERR_UNSUPPORTED;
 }
 
-// D = 256, bf16, 64 query rows per wave (256 per workgroup); use_wide decides when.
+// D = 256, bf16, 64 query rows per wave (256 per workgroup); plan_fwd decides when.
 template <bool PARTIAL>
 attn_status_t launch_fwd_wide(FwdArgs a, int B, int H, hipStream_t stream, const char* tag) {
   a.n_qtiles = (a.Tq + kBMW - 1) / kBMW;
@@ -127,21 +127,69 @@ int device_cus() {
   return cached[dev];
 }
 
-// Which D = 256 bf16 forward kernel a launch takes.  The 64-row kernel does about 8% more
-// work per unit time than the 32-row one, but its workgroups are twice as large, so the
-// last wave of workgroups is emptier: it is taken when its waves, each worth 2 / 1.08 of a
-// 32-row wave, come to fewer.  ATTN_PREFIX_FWD_ROWS=128 or 256 forces either kernel.
-bool use_wide(int D, attn_dtype_t dtype, int B, int H, int Tq) {
-  if (dtype != ATTN_BF16 || D != 256) return false;
+// Which D = 256 bf16 forward path a launch takes: the 32-row kernel, the 64-row kernel,
+// or both in one grid (the 64-row path for the rows that fill whole rounds of the GPU, the
+// 32-row path for the rest).  The 64-row path does about 8% more work per unit time, but
+// its workgroups are twice as tall, so a last, partly filled round of them costs more.
+// Each choice is costed in rounds of workgroups over the device's CUs, a 64-row round
+// counting 2 / 1.08 of a 32-row one, and the cheapest is taken (ties to the simpler).
+// ATTN_PREFIX_FWD_ROWS=128, 256 or mixed forces a choice (mixed: every full 256-row tile
+// on the 64-row path).
+struct FwdPlan {
+  int kind;        // 0: 32-row kernel, 1: 64-row kernel, 2: mixed
+  int wide_tiles;  // mixed: 256-row tiles per head on the 64-row path
+};
+
+FwdPlan plan_fwd(int D, attn_dtype_t dtype, int B, int H, int Tq) {
+  FwdPlan p{0, 0};
+  if (dtype != ATTN_BF16 || D != 256) return p;
   const char* e = getenv("ATTN_PREFIX_FWD_ROWS");
-  if (e && strcmp(e, "256") == 0) return true;
-  if (e && strcmp(e, "128") == 0) return false;
-  if (Tq <= kBM) return false;
-  const int64_t cus = device_cus();
   const int64_t heads = (int64_t)B * H;
-  const int64_t waves_narrow = (heads * ((Tq + kBM - 1) / kBM) + cus - 1) / cus;
-  const int64_t waves_wide = (heads * ((Tq + kBMW - 1) / kBMW) + cus - 1) / cus;
-  return waves_wide * 200 < waves_narrow * 108;
+  const int64_t full_w = Tq / kBMW;  // full 256-row tiles per head
+  if (e && strcmp(e, "128") == 0) return p;
+  if (e && strcmp(e, "256") == 0) return FwdPlan{1, 0};
+  if (e && strcmp(e, "mixed") == 0) {
+    if (full_w == 0) return p;
+    if (full_w * kBMW == Tq) return FwdPlan{1, 0};
+    return FwdPlan{2, (int)full_w};
+  }
+  if (Tq <= kBM) return p;
+  const int64_t cus = device_cus();
+  auto rounds = [&](int64_t wgs) { return (wgs + cus - 1) / cus; };
+  // costs in hundredths of a 32-row round
+  const int64_t c_narrow = rounds(heads * ((Tq + kBM - 1) / kBM)) * 108;
+  const int64_t c_wide = rounds(heads * ((Tq + kBMW - 1) / kBMW)) * 200;
+  FwdPlan best = c_wide < c_narrow ? FwdPlan{1, 0} : p;
+  int64_t c_best = c_wide < c_narrow ? c_wide : c_narrow;
+  const int64_t w_rounds = heads * full_w / cus;  // whole rounds of full 256-row tiles
+  if (w_rounds >= 1) {
+    const int64_t W = (w_rounds * cus) / heads < full_w ? (w_rounds * cus) / heads : full_w;
+    const int64_t rest = Tq - W * kBMW;
+    if (W >= 1 && rest > 0) {
+      const int64_t c_mixed = rounds(heads * W) * 200 + rounds(heads * ((rest + kBM - 1) / kBM)) * 108;
+      if (c_mixed < c_best) best = FwdPlan{2, (int)W};
+    }
+  }
+  return best;
+}
+
+// Both paths in one grid: the 64-row one over rows [0, 256 W) of every head, the 32-row
+// one over the rest.
+attn_status_t launch_fwd_mixed(const FwdArgs& base, int B, int H, int W, hipStream_t stream) {
+  FwdArgs wide = base, narrow = base;
+  wide.n_qtiles = W;
+  narrow.row_base = W * kBMW;
+  narrow.n_qtiles = (base.Tq - narrow.row_base + kBM - 1) / kBM;
+  const int64_t n_wide = (int64_t)W * B * H;
+  narrow.wg_base = (int)n_wide;
+  const int64_t grid = n_wide + (int64_t)narrow.n_qtiles * B * H;
+  if (verbose())
+    fprintf(stderr, "[attn_prefix] prefix_fwd D=256 bf16 mixed grid=%lld (64-row %lld, 32-row %lld) lds=%d\n",
+            (long long)grid, (long long)n_wide, (long long)(grid - n_wide), Bf16Dma<256>::LDS_BYTES);
+  (void)hipGetLastError();
+  hipLaunchKernelGGL(attn_fwd_mixed_kernel, dim3((unsigned)grid), dim3(kThreads), 0, stream, wide, narrow,
+                     (int)n_wide);
+  return hipGetLastError() == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
 }
 
 // WPE_DKDV = 0 selects the cross-tile pipelined dk/dv kernel (one wave per SIMD), otherwise
@@ -278,7 +326,9 @@ attn_status_t attn_prefix_fwd(const void* q, const void* k, const void* v, const
   a.n_qtiles = (Tq + kBM - 1) / kBM;
   a.out = out;
   a.lse = lse;
-  if (use_wide(D, dtype, B, H, Tq)) return launch_fwd_wide<false>(a, B, H, reinterpret_cast<hipStream_t>(stream), "prefix_fwd");
+  const FwdPlan plan = plan_fwd(D, dtype, B, H, Tq);
+  if (plan.kind == 1) return launch_fwd_wide<false>(a, B, H, reinterpret_cast<hipStream_t>(stream), "prefix_fwd");
+  if (plan.kind == 2) return launch_fwd_mixed(a, B, H, plan.wide_tiles, reinterpret_cast<hipStream_t>(stream));
   const int64_t grid = (int64_t)a.n_qtiles * B * H;
   return dispatch_fwd<false>(a, D, dtype, grid, reinterpret_cast<hipStream_t>(stream));
 }

@@ -65,6 +65,8 @@ struct FwdArgs {
   float* part_out;   // split mode: [B,H,C,Tq,D]
   float* part_lse;   // split mode: [B,H,C,Tq]
   int32_t* counters; // single-launch split mode: [B,H,n_qtiles] arrival counts, zero between launches
+  int wg_base;        // workgroups of this part start at blockIdx.x = wg_base (a launch split
+  int row_base;       // between two kernels' paths); its query rows start at row_base
 };
 
 __device__ __forceinline__ float pair_max(float x) {
@@ -407,7 +409,7 @@ struct Work {
 template <bool PARTIAL>
 __device__ __forceinline__ Work decode(const FwdArgs& a, int tile_rows, int local_row) {
   Work w;
-  int wg = blockIdx.x;
+  int wg = (int)blockIdx.x - a.wg_base;
   const int qt = wg % a.n_qtiles;
   wg /= a.n_qtiles;
   w.c = 0;
@@ -426,7 +428,7 @@ __device__ __forceinline__ Work decode(const FwdArgs& a, int tile_rows, int loca
     w.hi = min(w.lo + a.chunk, n);
   }
   w.bh = (int64_t)w.b * a.H + w.h;
-  w.row = qt * tile_rows + local_row;
+  w.row = a.row_base + qt * tile_rows + local_row;
   w.row_ok = w.row < a.Tq;
   w.out_row = PARTIAL ? ((w.bh * a.C + w.c) * a.Tq + w.row) : (w.bh * a.Tq + w.row);
   return w;
@@ -1307,12 +1309,25 @@ __device__ __forceinline__ void splitkv_merge_tail(const FwdArgs& a) {
   if (threadIdx.x == 0) a.counters[cidx] = 0;
 }
 
-// 64 query rows per wave at D = 256, bf16 (the host picks it by the wave count, see use_wide).
+// 64 query rows per wave at D = 256, bf16 (the host picks it by the wave count, see plan_fwd).
 template <bool PARTIAL, bool STREAM>
 __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads), amdgpu_waves_per_eu(1, 1)))
 void attn_fwd_wide_kernel(FwdArgs a) {
   __shared__ __attribute__((aligned(16))) char smem[WideLayout::LDS_BYTES];
   bf16_fwd_wide<PARTIAL, STREAM>(a, smem);
+}
+
+// bf16 D = 256 launches split between the two paths in one grid: workgroups
+// [0, n_wide) take the 64-row path over the rows that fill whole rounds of the GPU
+// (wide.n_qtiles tiles of 256 per head), the rest the 32-row path over the remaining
+// rows (narrow.row_base ..).  The workgroups of a launch then fill the machine more
+// evenly than either kernel alone (e.g. 2 + 1 rounds instead of 2.5 or 5).
+__global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads), amdgpu_waves_per_eu(1, 1)))
+void attn_fwd_mixed_kernel(FwdArgs wide, FwdArgs narrow, int n_wide) {
+  static_assert(WideLayout::LDS_BYTES <= Bf16Dma<256>::LDS_BYTES, "one LDS allocation serves both paths");
+  __shared__ __attribute__((aligned(16))) char smem[Bf16Dma<256>::LDS_BYTES];
+  if ((int)blockIdx.x < n_wide) bf16_fwd_wide<false, false>(wide, smem);
+  else bf16_fwd_dma<256, false, false>(narrow, smem);
 }
 
 template <class P, int D, bool PARTIAL, int WAVES_PER_EU, bool STREAM, bool MERGE = false>

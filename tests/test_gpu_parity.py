@@ -37,23 +37,27 @@ def _oracle(q, k, v, kv, scale):
     return ref_prefix_fwd(_np(q), _np(k), _np(v), kv.cpu().numpy(), scale)
 
 
-@pytest.fixture(params=[128, 256])
+@pytest.fixture(params=[128, 256, "mixed"])
 def fwd_rows(request, monkeypatch):
-    """Force the bf16 D = 256 forward kernel: 32 query rows per wave (128 per workgroup) or
-    64 (256 per workgroup).  Other head dims have one kernel; their 256 case is skipped."""
+    """Force the bf16 D = 256 forward path: 32 query rows per wave (128 per workgroup), 64
+    (256 per workgroup), or both in one grid (every full 256-row tile on the 64-row path, the
+    remaining rows on the 32-row one).  Other head dims have one kernel: their 256 and mixed
+    cases are skipped, as is mixed where no 256-row tile is full or none is left over."""
     monkeypatch.setenv("ATTN_PREFIX_FWD_ROWS", str(request.param))
     return request.param
 
 
-def _skip_dup(D, rows):
-    if D != 256 and rows == 256:
+def _skip_dup(D, rows, Tq=None):
+    if D != 256 and rows != 128:
         pytest.skip("one bf16 forward kernel at this head dim")
+    if rows == "mixed" and (Tq is None or Tq < 256 or Tq % 256 == 0):
+        pytest.skip("mixed is one of the two kernels at this T_q")
 
 
 @pytest.mark.parametrize("D", [64, 128, 256])
 @pytest.mark.parametrize("Tq", [1, 17, 128, 129])
 def test_edge_matrix_bf16(D, Tq, fwd_rows):
-    _skip_dup(D, fwd_rows)
+    _skip_dup(D, fwd_rows, Tq)
     S = 200
     lens = [0, 1, 63, 64, 65, S]
     log(f"edge bf16 D={D} Tq={Tq} S={S} lens={lens} rows={fwd_rows}")
@@ -67,7 +71,7 @@ def test_edge_matrix_bf16(D, Tq, fwd_rows):
 @pytest.mark.parametrize("D", [64, 128, 256])
 def test_multi_tile_bf16_sharp(D, fwd_rows):
     """Several query and key tiles, ragged tails, peaky attention (q scaled x4)."""
-    _skip_dup(D, fwd_rows)
+    _skip_dup(D, fwd_rows, 300)
     B, H, Tq, S = 2, 3, 300, 777
     lens = [700, 777]
     log(f"sharp bf16 D={D}")
@@ -160,7 +164,7 @@ def test_combine_edge_cases():
 @pytest.mark.parametrize("D", [128, 256])
 def test_padding_invariance_bitwise(D, fwd_rows):
     """Pads never read: no pads, +-1e4 pads and NaN pads give identical bits."""
-    _skip_dup(D, fwd_rows)
+    _skip_dup(D, fwd_rows, 70)
     B, H, Tq, n = 2, 2, 70, 333
     log(f"padding invariance D={D}")
     q, k, v, kv = make_inputs(B, H, Tq, n, D, [n, 129], "bf16", 1.0, seed=500 + D, device=DEV)
@@ -183,6 +187,7 @@ def test_padding_invariance_bitwise(D, fwd_rows):
 
 
 def test_determinism_bitwise(fwd_rows):
+    _skip_dup(256, fwd_rows, 300)
     q, k, v, kv = make_inputs(2, 4, 300, 1000, 256, [1000, 517], "bf16", 0.7, seed=600, device=DEV)
     o1, l1 = _run_fused(q, k, v, kv, 0.0625)
     o2, l2 = _run_fused(q, k, v, kv, 0.0625)
@@ -279,6 +284,7 @@ def test_splitkv_other_head_dims(D):
 @pytest.mark.parametrize("scale", [-0.0625, 0.0, 0.9])
 def test_scale_sign_and_zero(scale, fwd_rows):
     """Negative scales (Q is negated internally), scale 0 (uniform weights) and a large scale."""
+    _skip_dup(256, fwd_rows, 130)
     D, B, H, Tq, S = 256, 2, 2, 130, 300
     lens = [300, 77]
     q, k, v, kv = make_inputs(B, H, Tq, S, D, lens, "bf16", 1.0, seed=1300, device=DEV)
@@ -315,6 +321,7 @@ def test_largest_key_slice(fwd_rows):
     offsets near the top of the range stay correct (both D = 256 kernels; with the 64-row
     one, the dominant last key of the second case also sends the workgroup through its
     second pass)."""
+    _skip_dup(256, fwd_rows, 64)
     D, S = 256, (1 << 22) - 64
     n = S - 5
     Tq = 64
@@ -418,3 +425,18 @@ def test_wide_one_row_takes_second_pass(monkeypatch):
     out, lse = _run_fused(q, k, v, kv, scale)
     ro, rl = _oracle(q, k, v, kv, scale)
     assert_parity(out, lse, ro, rl, "bf16", "wide one bad row")
+
+
+@pytest.mark.parametrize("Tq", [257, 300, 511, 700])
+def test_mixed_edge_matrix(Tq, monkeypatch):
+    """Both D = 256 paths in one grid: full 256-row tiles on the 64-row path, the rows after
+    them on the 32-row path (row bases past 0, workgroup bases past 0)."""
+    monkeypatch.setenv("ATTN_PREFIX_FWD_ROWS", "mixed")
+    D, S = 256, 200
+    lens = [0, 1, 31, 32, 33, 64, 65, S]
+    log(f"mixed edge Tq={Tq} lens={lens}")
+    q, k, v, kv = make_inputs(len(lens), 2, Tq, S, D, lens, "bf16", 1.0, seed=1800 + Tq, device=DEV)
+    scale = 1.0 / math.sqrt(D)
+    out, lse = _run_fused(q, k, v, kv, scale)
+    ro, rl = _oracle(q, k, v, kv, scale)
+    assert_parity(out, lse, ro, rl, "bf16", f"mixed edge Tq={Tq}")
