@@ -156,7 +156,7 @@ struct Bf16Dma {
   static constexpr int NBLK = kBN / RPB;   // blocks per tile (32, 16, 8)
   static constexpr int BLK = 1040;         // padded block stride
   static constexpr int TILE_BYTES = NBLK * BLK;
-  static constexpr int LDS_BYTES = 4 * TILE_BYTES + 16;  // K and V, two buffers each; 4 flags
+  static constexpr int LDS_BYTES = 4 * TILE_BYTES;  // K and V, two buffers each
   static constexpr int NQ = D / 16;
   static constexpr int LPR = ROWB / 16;    // DMA lanes per row
   static constexpr bool kIsF32 = false;
@@ -836,7 +836,8 @@ constexpr int kBNW = 32;   // keys per tile
 struct WideLayout {
   using P = Bf16Dma<256>;
   static constexpr int TILE_BYTES = 16 * P::BLK;
-  static constexpr int LDS_BYTES = 4 * TILE_BYTES;  // K and V, two buffers each
+  static constexpr int FLAGS = 4 * TILE_BYTES;         // K and V, two buffers each; then 4 flags
+  static constexpr int LDS_BYTES = FLAGS + 4 * 4;
   static constexpr int DMA_PER_WAVE = 4;            // 16 blocks per tile over 4 waves
   static_assert(P::key_of(15, 1) < kBNW && P::blk_of(kBNW - 1) < 16, "keys 0..31 fill blocks 0..15");
 
@@ -933,7 +934,9 @@ __device__ __forceinline__ void bf16_fwd_wide(const FwdArgs& a, char* smem_gener
   lds_char* const vbuf0 = smem + 2 * L::TILE_BYTES;
   lds_char* const vbuf1 = smem + 3 * L::TILE_BYTES;
   volatile __attribute__((address_space(3))) int* const bad_flag =
-      (volatile __attribute__((address_space(3))) int*)(smem + 4 * L::TILE_BYTES);  // one per wave
+      (volatile __attribute__((address_space(3))) int*)(smem + L::FLAGS);  // one per wave
+  static_assert(L::FLAGS >= 4 * L::TILE_BYTES && L::FLAGS + 4 * (int)sizeof(int) <= L::LDS_BYTES,
+                "the flags sit past the tile buffers, inside the allocation");
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
