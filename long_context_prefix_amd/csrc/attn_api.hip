@@ -7,6 +7,8 @@
 #include <stdlib.h>
 #include <string.h>
 
+#include <atomic>
+
 #include "attn_bwd_kernels.hpp"
 #include "attn_kernels.hpp"
 #include "attn_prefix.h"
@@ -20,13 +22,17 @@ constexpr int64_t kMaxI32 = 2147483647;
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
 
+// Lazily filled caches below are atomics: calls from several host threads may fill them
+// at once, each with the same value.
 bool verbose() {
-  static int v = -1;
-  if (v < 0) {
+  static std::atomic<int> v{-1};
+  int x = v.load(std::memory_order_relaxed);
+  if (x < 0) {
     const char* e = getenv("ATTN_PREFIX_VERBOSE");
-    v = (e && e[0] && e[0] != '0') ? 1 : 0;
+    x = (e && e[0] && e[0] != '0') ? 1 : 0;
+    v.store(x, std::memory_order_relaxed);
   }
-  return v == 1;
+  return x == 1;
 }
 
 int esize(attn_dtype_t dt) { return dt == ATTN_F32 ? 4 : 2; }
@@ -116,15 +122,15 @@ attn_status_t launch_fwd_wide(FwdArgs a, int B, int H, hipStream_t stream, const
 
 // Compute units of the current device (cached per device; 256 if the query fails).
 int device_cus() {
-  static int cached[64] = {0};
+  static std::atomic<int> cached[64];  // zero-initialized: not yet queried
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-  if (cached[dev] == 0) {
-    int n = 0;
+  int n = cached[dev].load(std::memory_order_relaxed);
+  if (n == 0) {
     if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
-    cached[dev] = n;
+    cached[dev].store(n, std::memory_order_relaxed);
   }
-  return cached[dev];
+  return n;
 }
 
 // Which D = 256 bf16 forward path a launch takes: the 32-row kernel, the 64-row kernel,
