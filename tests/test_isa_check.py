@@ -44,3 +44,43 @@ def test_built_library_assembly_is_clean():
     text = open(build.ASM).read()
     assert "v_mfma_f32_32x32x16_bf16 v[" in text  # the inline score MFMAs are present
     assert inline_mfma_hazards(text) == []
+
+
+AGPR_MFMA = "v_mfma_f32_32x32x16_bf16 a[16:31], v[2:5], v[6:9], a[16:31]"
+
+
+def _asm_a(*after, before=()):
+    return "\n".join(["_Zk:", *before, ";;#ASMSTART", AGPR_MFMA, ";;#ASMEND", *after])
+
+
+def test_early_accvgpr_read_of_an_agpr_result_is_found():
+    assert len(inline_mfma_hazards(_asm_a("v_accvgpr_read_b32 v40, a20"))) == 1
+    # an AGPR outside the result is fine
+    assert inline_mfma_hazards(_asm_a("v_accvgpr_read_b32 v40, a40")) == []
+
+
+def test_early_spill_of_an_agpr_result_is_found():
+    assert len(inline_mfma_hazards(_asm_a("scratch_store_dwordx4 off, a[16:19], off"))) == 1
+
+
+def test_early_overwrite_of_a_result_is_found():
+    assert len(inline_mfma_hazards(_asm_a("v_accvgpr_write_b32 a17, v3"))) == 1
+    assert len(inline_mfma_hazards(_asm("v_mov_b32 v12, 0"))) == 1  # VGPR result overwritten by VALU
+    assert len(inline_mfma_hazards(_asm("ds_read_b128 v[10:13], v1"))) == 1  # ... or by a load
+
+
+def test_guarded_agpr_read_is_clean():
+    asm = _asm_a("s_nop 7", "s_nop 7", "s_nop 7", "v_accvgpr_read_b32 v40, a20")
+    assert inline_mfma_hazards(asm) == []
+
+
+def test_operand_written_just_before_an_inline_mfma_is_found():
+    # a VALU write of the B operand right before the MFMA
+    assert len(inline_mfma_hazards(_asm_a(before=("v_cvt_pk_bf16_f32 v7, v40, v41",)))) == 1
+    # of the accumulator (an AGPR) through v_accvgpr_write
+    assert len(inline_mfma_hazards(_asm_a(before=("v_accvgpr_write_b32 a16, v3",)))) == 1
+    # four wait states in between are enough
+    asm = _asm_a(before=("v_cvt_pk_bf16_f32 v7, v40, v41", "s_nop 3"))
+    assert inline_mfma_hazards(asm) == []
+    # an unrelated write is fine
+    assert inline_mfma_hazards(_asm_a(before=("v_cvt_pk_bf16_f32 v70, v40, v41",))) == []
