@@ -458,6 +458,48 @@ __device__ __forceinline__ void write_rows(const FwdArgs& a, const Work& w, cons
   }
 }
 
+// Partial rows of one wave through LDS: the wave's 32 rows are staged row-major
+// (16-byte unit u of row r at unit u ^ (r mod D/4), so that neither the writes,
+// one unit per lane in 32 rows, nor the reads, whole rows, meet a bank twice),
+// then each store instruction writes 1 KB of consecutive rows.  The rows of a
+// workgroup are consecutive in part_out, so the stores cover whole cache lines
+// instead of 32-byte pieces of 32 rows, and they are issued at device scope and
+// non-temporal (cache policy sc1 nt): written through the XCD's L2 rather than
+// left there dirty among the streaming tile loads.  On MI355X this took the
+// split-KV partial at the inducing shape from 6.2 to 5.6 ms; whole-line stores
+// with the default policy, or 32-byte pieces with any policy, measured no gain.
+constexpr int kCpolSc1Nt = 16 | 2;  // buffer-store cache policy bits: sc1 (device scope), nt
+
+template <int D>
+__device__ __forceinline__ void write_partial_staged(const FwdArgs& a, const Work& w, const f32x16 (&o)[D / 32],
+                                                     float inv_l, float lse_nat, int h_half, lds_char* stage,
+                                                     int lane) {
+  constexpr int U = D / 4;  // 16-byte units per row
+  const int r = lane & 31;
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+    for (int rg = 0; rg < 4; ++rg) {
+      const int u = 8 * db + 2 * rg + h_half;
+      const f32x4 x = {o[db][4 * rg + 0] * inv_l, o[db][4 * rg + 1] * inv_l, o[db][4 * rg + 2] * inv_l,
+                       o[db][4 * rg + 3] * inv_l};
+      *reinterpret_cast<__attribute__((address_space(3))) f32x4*>(stage + (r * U + (u ^ (r & (U - 1)))) * 16) = x;
+    }
+  // the wave's rows [row0, row0 + 32) are rows out0.. of part_out; rows at or past Tq lie
+  // outside the resource, so their stores are dropped
+  const int row0 = w.row - r;
+  const int nrows = min(max(a.Tq - row0, 0), 32);
+  const __amdgpu_buffer_rsrc_t rs = make_rsrc(a.part_out + (w.out_row - r) * D, (uint32_t)(nrows * D * 4));
+#pragma unroll
+  for (int k = 0; k < 32 * U / 64; ++k) {
+    const int idx = 64 * k + lane, rr = idx / U, c = idx % U;
+    const f32x4 x = *reinterpret_cast<const __attribute__((address_space(3))) f32x4*>(
+        stage + (rr * U + (c ^ (rr & (U - 1)))) * 16);
+    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, x), rs, (uint32_t)(idx * 16), 0, kCpolSc1Nt);
+  }
+  if (h_half == 0 && w.row_ok) a.part_lse[w.out_row] = lse_nat;
+}
+
 template <class P, int D, bool PARTIAL>
 __device__ __forceinline__ void write_empty(const FwdArgs& a, const Work& w, int h_half) {
   f32x16 z[D / 32];
@@ -814,7 +856,14 @@ __device__ __forceinline__ void bf16_fwd_dma(const FwdArgs& a, char* smem_generi
   P::accumulate(o, pk, ((T - 1) & 1) ? vbuf1 : vbuf0, vbase);
 
   const float l = pair_sum(sm.l);
-  write_rows<P, D, PARTIAL>(a, w, o, 1.0f / l, (sm.m + __builtin_amdgcn_logf(l)) * kLn2, h_half);
+  if constexpr (PARTIAL && STREAM) {
+    static_assert(4 * 32 * D * 4 <= P::LDS_BYTES, "four waves' partial rows fit the tile buffers");
+    lds_barrier();  // every wave is done with the last V tile: the buffers take the partial rows
+    write_partial_staged<D>(a, w, o, 1.0f / l, (sm.m + __builtin_amdgcn_logf(l)) * kLn2, h_half,
+                            smem + wave * (32 * D * 4), lane);
+  } else {
+    write_rows<P, D, PARTIAL>(a, w, o, 1.0f / l, (sm.m + __builtin_amdgcn_logf(l)) * kLn2, h_half);
+  }
 }
 
 // ------------------------------------------------ bf16, D = 256, 64 rows per wave
@@ -1195,49 +1244,78 @@ __device__ __forceinline__ void bf16_fwd_wide(const FwdArgs& a, char* smem_gener
 // of the row (stride Tq between chunks), po at O_0 of the thread's columns
 // (stride Tq * D).  Shared by the combine kernel and the single-launch split path
 // so that both produce the same bits.
+constexpr int kMergeRegs = 32;  // chunk counts up to this are merged from registers in one pass of loads
+
 template <int D, bool OUT_F32>
 __device__ __forceinline__ void merge_row4(const float* pl, const float* po, int C, int Tq, void* out, float* lse,
                                            int64_t row, int col) {
-  // eight chunks' loads in flight at a time; the sums still run in chunk order
-  constexpr int U = 8;
-  float mx = -__builtin_inff();
-  {
-    int c = 0;
-    for (; c + U <= C; c += U) {
-      float lc[U];
-#pragma unroll
-      for (int u = 0; u < U; ++u) lc[u] = pl[(int64_t)(c + u) * Tq];
-#pragma unroll
-      for (int u = 0; u < U; ++u) mx = fmaxf(mx, lc[u]);
-    }
-    for (; c < C; ++c) mx = fmaxf(mx, pl[(int64_t)c * Tq]);
-  }
-
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
   float wsum = 0.f;
-  if (mx != -__builtin_inff()) {
-    int c = 0;
-    for (; c + U <= C; c += U) {
-      f32x4 x[U];
-      float lc[U];
+  float mx = -__builtin_inff();
+  if (C <= kMergeRegs) {
+    // every chunk's statistic and partial in flight at once (one memory round trip per row);
+    // the max, the weights and the sums are then taken in chunk order, as below
+    float lc[kMergeRegs];
+    f32x4 x[kMergeRegs];
 #pragma unroll
-      for (int u = 0; u < U; ++u) {
-        lc[u] = pl[(int64_t)(c + u) * Tq];
-        x[u] = *reinterpret_cast<const f32x4*>(po + (int64_t)(c + u) * Tq * D);
+    for (int u = 0; u < kMergeRegs; ++u) {
+      lc[u] = -__builtin_inff();
+      x[u] = f32x4{0.f, 0.f, 0.f, 0.f};
+      if (u < C) {
+        lc[u] = pl[(int64_t)u * Tq];
+        x[u] = *reinterpret_cast<const f32x4*>(po + (int64_t)u * Tq * D);
       }
+    }
 #pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const float w = __builtin_amdgcn_exp2f((lc[u] - mx) * kLog2e);
+    for (int u = 0; u < kMergeRegs; ++u) mx = fmaxf(mx, lc[u]);
+    if (mx != -__builtin_inff()) {
+#pragma unroll
+      for (int u = 0; u < kMergeRegs; ++u)
+        if (u < C) {
+          const float w = __builtin_amdgcn_exp2f((lc[u] - mx) * kLog2e);
+          wsum += w;
+          acc += w * x[u];
+        }
+      acc *= 1.0f / wsum;
+    }
+  } else {
+    // eight chunks' loads in flight at a time; the sums still run in chunk order
+    constexpr int U = 8;
+    {
+      int c = 0;
+      for (; c + U <= C; c += U) {
+        float lc[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) lc[u] = pl[(int64_t)(c + u) * Tq];
+#pragma unroll
+        for (int u = 0; u < U; ++u) mx = fmaxf(mx, lc[u]);
+      }
+      for (; c < C; ++c) mx = fmaxf(mx, pl[(int64_t)c * Tq]);
+    }
+    if (mx != -__builtin_inff()) {
+      int c = 0;
+      for (; c + U <= C; c += U) {
+        f32x4 x[U];
+        float lc[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          lc[u] = pl[(int64_t)(c + u) * Tq];
+          x[u] = *reinterpret_cast<const f32x4*>(po + (int64_t)(c + u) * Tq * D);
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          const float w = __builtin_amdgcn_exp2f((lc[u] - mx) * kLog2e);
+          wsum += w;
+          acc += w * x[u];
+        }
+      }
+      for (; c < C; ++c) {
+        const float w = __builtin_amdgcn_exp2f((pl[(int64_t)c * Tq] - mx) * kLog2e);
         wsum += w;
-        acc += w * x[u];
+        acc += w * *reinterpret_cast<const f32x4*>(po + (int64_t)c * Tq * D);
       }
+      acc *= 1.0f / wsum;
     }
-    for (; c < C; ++c) {
-      const float w = __builtin_amdgcn_exp2f((pl[(int64_t)c * Tq] - mx) * kLog2e);
-      wsum += w;
-      acc += w * *reinterpret_cast<const f32x4*>(po + (int64_t)c * Tq * D);
-    }
-    acc *= 1.0f / wsum;
   }
   const int64_t off = row * D + col;
   if (OUT_F32) {
@@ -1259,7 +1337,6 @@ struct CombineArgs {
   void* out;
   float* lse;
 };
-
 template <int D, bool OUT_F32>
 __global__ __attribute__((amdgpu_flat_work_group_size(256, 256)))
 void lse_combine_kernel(CombineArgs a) {

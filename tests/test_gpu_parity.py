@@ -106,11 +106,12 @@ def test_tiny_prefix_mask_workload():
 
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
 @pytest.mark.parametrize("chunk", [64, 128, 192])
-def test_splitkv_partial_and_combine(dtype, chunk):
+@pytest.mark.parametrize("Tq", [130, 100])  # 100: one query tile per head (the streaming launch)
+def test_splitkv_partial_and_combine(dtype, chunk, Tq):
     D = 128
-    B, H, Tq, S = 3, 2, 130, 450
+    B, H, S = 3, 2, 450
     lens = [0, 129, 450]
-    log(f"splitkv dtype={dtype} chunk={chunk}")
+    log(f"splitkv dtype={dtype} chunk={chunk} Tq={Tq}")
     q, k, v, kv = make_inputs(B, H, Tq, S, D, lens, dtype, 1.0, seed=400 + chunk, device=DEV)
     scale = 1.0 / math.sqrt(D)
     po, pl = _lib.attn_splitkv_partial(q, k, v, kv, chunk, scale)
@@ -221,8 +222,12 @@ def test_kv_len_out_of_range_is_clamped():
     assert_parity(out, lse, ro, rl, "bf16", "clamped kv_len")
 
 
-def test_guard_bytes_untouched():
-    B, H, Tq, S, D = 2, 2, 130, 300, 128
+@pytest.mark.parametrize("Tq,D", [(130, 128), (17, 128), (45, 64), (100, 256)])
+def test_guard_bytes_untouched(Tq, D):
+    """Nothing is written past any output, also when a wave's 32 rows run past T_q
+    (one query tile per head: partial rows are then written whole rows at a time)."""
+    B, H, S = 2, 2, 300
+    log(f"guard bytes Tq={Tq} D={D}")
     q, k, v, kv = make_inputs(B, H, Tq, S, D, [300, 65], "bf16", 1.0, seed=1000, device=DEV)
     G = 4096
     n_out, n_lse = B * H * Tq * D, B * H * Tq
