@@ -88,8 +88,10 @@ int attn_version(void);
  *   lse      : device fp32 [B,H,Tq] natural-log LSE, or NULL to skip it
  * For bf16 at D = 256 the library picks one of two kernels (32 or 64 query rows
  * per wavefront), or both in one grid, from the launch shape and the device's
- * compute-unit count; results differ only in summation order.  The environment
- * variable ATTN_PREFIX_FWD_ROWS=128, 256 or mixed forces a choice (testing).
+ * compute-unit count; results differ only in summation order.  At D = 128 it
+ * takes the 32-row kernel.  The environment variable ATTN_PREFIX_FWD_ROWS=128,
+ * 256 or mixed forces a choice (testing; 256 also applies at D = 128, mixed
+ * only at D = 256).
  */
 attn_status_t attn_prefix_fwd(const void* q, const void* k, const void* v, const int32_t* kv_len,
                               int B, int H, int Tq, int S, int D, float scale, attn_dtype_t dtype,

@@ -103,20 +103,20 @@ attn_status_t dispatch_fwd(const FwdArgs& a, int D, attn_dtype_t dtype, int64_t 
   return ATTN_ERR_UNSUPPORTED;
 }
 
-// D = 256, bf16, 64 query rows per wave (256 per workgroup); plan_fwd decides when.
-template <bool PARTIAL>
+// D = 256 or 128, bf16, 64 query rows per wave (256 per workgroup); plan_fwd decides when.
+template <int D, bool PARTIAL>
 attn_status_t launch_fwd_wide(FwdArgs a, int B, int H, hipStream_t stream, const char* tag) {
   a.n_qtiles = (a.Tq + kBMW - 1) / kBMW;
   const int64_t grid = (int64_t)a.n_qtiles * B * H * (PARTIAL ? a.C : 1);
   const bool stream_kv = a.n_qtiles == 1;
   if (verbose())
-    fprintf(stderr, "[attn_prefix] %s D=256 bf16 wide grid=%lld block=%d lds=%d%s\n", tag, (long long)grid, kThreads,
-            WideLayout::LDS_BYTES, stream_kv ? " streaming" : "");
+    fprintf(stderr, "[attn_prefix] %s D=%d bf16 wide grid=%lld block=%d lds=%d%s\n", tag, D, (long long)grid, kThreads,
+            WideLayout<D>::LDS_BYTES, stream_kv ? " streaming" : "");
   (void)hipGetLastError();
   if (stream_kv)
-    hipLaunchKernelGGL((attn_fwd_wide_kernel<PARTIAL, true>), dim3((unsigned)grid), dim3(kThreads), 0, stream, a);
+    hipLaunchKernelGGL((attn_fwd_wide_kernel<D, PARTIAL, true>), dim3((unsigned)grid), dim3(kThreads), 0, stream, a);
   else
-    hipLaunchKernelGGL((attn_fwd_wide_kernel<PARTIAL, false>), dim3((unsigned)grid), dim3(kThreads), 0, stream, a);
+    hipLaunchKernelGGL((attn_fwd_wide_kernel<D, PARTIAL, false>), dim3((unsigned)grid), dim3(kThreads), 0, stream, a);
   return hipGetLastError() == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
 }
 
@@ -140,7 +140,9 @@ int device_cus() {
 // Each choice is costed in rounds of workgroups over the device's CUs, a 64-row round
 // counting 2 / 1.08 of a 32-row one, and the cheapest is taken (ties to the simpler).
 // ATTN_PREFIX_FWD_ROWS=128, 256 or mixed forces a choice (mixed: every full 256-row tile
-// on the 64-row path).
+// on the 64-row path).  At D = 128 the 64-row kernel is as fast as the 32-row one, not
+// faster (its MFMAs wait on the softmax VALU work, which at D = 128 is twice as dense per
+// MFMA), so it runs only when ATTN_PREFIX_FWD_ROWS=256 forces it.
 struct FwdPlan {
   int kind;        // 0: 32-row kernel, 1: 64-row kernel, 2: mixed
   int wide_tiles;  // mixed: 256-row tiles per head on the 64-row path
@@ -148,8 +150,9 @@ struct FwdPlan {
 
 FwdPlan plan_fwd(int D, attn_dtype_t dtype, int B, int H, int Tq) {
   FwdPlan p{0, 0};
-  if (dtype != ATTN_BF16 || D != 256) return p;
+  if (dtype != ATTN_BF16 || (D != 256 && D != 128)) return p;
   const char* e = getenv("ATTN_PREFIX_FWD_ROWS");
+  if (D == 128) return (e && strcmp(e, "256") == 0) ? FwdPlan{1, 0} : p;
   const int64_t heads = (int64_t)B * H;
   const int64_t full_w = Tq / kBMW;  // full 256-row tiles per head
   if (e && strcmp(e, "128") == 0) return p;
@@ -333,7 +336,9 @@ attn_status_t attn_prefix_fwd(const void* q, const void* k, const void* v, const
   a.out = out;
   a.lse = lse;
   const FwdPlan plan = plan_fwd(D, dtype, B, H, Tq);
-  if (plan.kind == 1) return launch_fwd_wide<false>(a, B, H, reinterpret_cast<hipStream_t>(stream), "prefix_fwd");
+  if (plan.kind == 1)
+    return D == 128 ? launch_fwd_wide<128, false>(a, B, H, reinterpret_cast<hipStream_t>(stream), "prefix_fwd")
+                    : launch_fwd_wide<256, false>(a, B, H, reinterpret_cast<hipStream_t>(stream), "prefix_fwd");
   if (plan.kind == 2) return launch_fwd_mixed(a, B, H, plan.wide_tiles, reinterpret_cast<hipStream_t>(stream));
   const int64_t grid = (int64_t)a.n_qtiles * B * H;
   return dispatch_fwd<false>(a, D, dtype, grid, reinterpret_cast<hipStream_t>(stream));

@@ -882,17 +882,27 @@ __device__ __forceinline__ void bf16_fwd_dma(const FwdArgs& a, char* smem_generi
 constexpr int kBMW = 256;  // query rows per workgroup (64 per wave)
 constexpr int kBNW = 32;   // keys per tile
 
-struct WideLayout {
+template <int D>
+struct WideLayout;
+
+// D = 256: a 32-key tile is the first 16 blocks of the 64-key layout of Bf16Dma<256>
+// (keys 0..31), so the operand reads and the DMA are those of that layout.
+template <>
+struct WideLayout<256> {
   using P = Bf16Dma<256>;
+  static constexpr int SUB = 1;                        // 32-key tiles per DMA tile
   static constexpr int TILE_BYTES = 16 * P::BLK;
   static constexpr int FLAGS = 4 * TILE_BYTES;         // K and V, two buffers each; then 4 flags
   static constexpr int LDS_BYTES = FLAGS + 4 * 4;
   static constexpr int DMA_PER_WAVE = 4;            // 16 blocks per tile over 4 waves
+  static constexpr int HALF_OFF = 0;                // unused: one 32-key tile per buffer
   static_assert(P::key_of(15, 1) < kBNW && P::blk_of(kBNW - 1) < 16, "keys 0..31 fill blocks 0..15");
 
-  // Block b = wave + 4 bi of a tile, as Bf16Dma<256>::dma_block.  The lane's part of the
-  // global offset (row r = lane / 32, chunk lane % 32) is one VGPR for every block; the
-  // block's part, 512 key_of(b, 0), is added into a temporary inside the asm so that no
+  // the lane's part of the DMA offset (row lane / 32, chunk lane % 32), one VGPR for every block
+  __device__ static uint32_t dma_arg(int lane) { return (uint32_t)((lane >> 5) * 16 * (256 * 2) + (lane & 31) * 16); }
+
+  // Block b = wave + 4 bi of a tile, as Bf16Dma<256>::dma_block.  The block's part of the
+  // global offset, 512 key_of(b, 0), is added into a temporary inside the asm so that no
   // per-block offset stays live, and so that the whole offset is the VGPR offset that the
   // buffer range check sees.
   template <bool STREAM>
@@ -913,6 +923,29 @@ struct WideLayout {
           : "=&v"(t)
           : "v"(voff), "s"(boff), "s"(lds), "s"(rs)
           : "m0");
+  }
+};
+
+// D = 128: the DMA moves whole 64-key tiles of the Bf16Dma<128> layout, each holding two
+// 32-key tiles.  Keys 32..63 of that layout sit two rows below keys 0..31 in the same
+// blocks, so every operand address of the second 32-key tile is the first's plus 512
+// bytes (HALF_OFF), with the same bank pattern.
+template <>
+struct WideLayout<128> {
+  using P = Bf16Dma<128>;
+  static constexpr int SUB = 2;
+  static constexpr int TILE_BYTES = P::TILE_BYTES;
+  static constexpr int FLAGS = 4 * TILE_BYTES;
+  static constexpr int LDS_BYTES = FLAGS + 4 * 4;
+  static constexpr int DMA_PER_WAVE = P::DMA_PER_WAVE;
+  static constexpr int HALF_OFF = 2 * P::ROWB;
+  static_assert(P::addr(32, 0) - P::addr(0, 0) == HALF_OFF && P::addr(63, 0) - P::addr(31, 0) == HALF_OFF,
+                "keys 32..63 sit HALF_OFF bytes past keys 0..31");
+
+  __device__ static uint32_t dma_arg(int lane) { return (uint32_t)lane; }
+  template <bool STREAM>
+  __device__ static void dma_block(__amdgpu_buffer_rsrc_t rs, lds_char* buf, int wave_u, uint32_t lane, int bi) {
+    P::template dma_block<STREAM>(rs, buf, wave_u, (int)lane, bi);
   }
 };
 
@@ -972,11 +1005,15 @@ struct WideSoftmax {
   bool bad = false;  // some tile of this wave broke the slack in this pass
 };
 
-template <bool PARTIAL, bool STREAM>
+template <int D, bool PARTIAL, bool STREAM>
 __device__ __forceinline__ void bf16_fwd_wide(const FwdArgs& a, char* smem_generic) {
-  constexpr int D = 256;
-  using P = Bf16Dma<256>;
-  using L = WideLayout;
+  using P = Bf16Dma<D>;
+  using L = WideLayout<D>;
+  constexpr int SUB = L::SUB;         // 32-key tiles per DMA tile (1 at D = 256, 2 at D = 128)
+  constexpr int NF = P::NQ;           // K fragments (and V fragments) per 32-key tile: D / 16
+  constexpr int SPE = 2 * NF / 16;    // slots per softmax element: 2 at D = 256, 1 at D = 128
+  constexpr int NOB = D / 32;         // O blocks per group
+  constexpr int TK = kBNW * SUB;      // keys per DMA tile
   lds_char* const smem = (lds_char*)smem_generic;
   lds_char* const kbuf0 = smem;
   lds_char* const kbuf1 = smem + L::TILE_BYTES;
@@ -999,17 +1036,22 @@ __device__ __forceinline__ void bf16_fwd_wide(const FwdArgs& a, char* smem_gener
     write_empty<P, D, PARTIAL>(a, w[1], h_half);
     return;
   }
-  const uint32_t dma_voff = (uint32_t)((lane >> 5) * 16 * (D * 2) + (lane & 31) * 16);
+  const uint32_t dma_voff = L::dma_arg(lane);
   const int nkeys = w[0].hi - w[0].lo;
-  const int T = (nkeys + kBNW - 1) / kBNW;
+  const int T = (nkeys + kBNW - 1) / kBNW;  // 32-key tiles
   auto nv_of = [&](int t) {
     const int r = nkeys - t * kBNW;
     return r < 0 ? 0 : (r > kBNW ? kBNW : r);
   };
+  auto nd_of = [&](int m) {  // valid keys of DMA tile m
+    const int r = nkeys - m * TK;
+    return r < 0 ? 0 : (r > TK ? TK : r);
+  };
   const uint16_t* kg = reinterpret_cast<const uint16_t*>(a.k) + (w[0].bh * a.S + w[0].lo) * D;
   const uint16_t* vg = reinterpret_cast<const uint16_t*>(a.v) + (w[0].bh * a.S + w[0].lo) * D;
-  auto k_tile = [&](int t) { return make_rsrc(kg + (int64_t)t * kBNW * D, (uint32_t)nv_of(t) * (D * 2)); };
-  auto v_tile = [&](int t) { return make_rsrc(vg + (int64_t)t * kBNW * D, (uint32_t)nv_of(t) * (D * 2)); };
+  // resources over the valid rows of DMA tile m only
+  auto k_tile = [&](int m) { return make_rsrc(kg + (int64_t)m * TK * D, (uint32_t)nd_of(m) * (D * 2)); };
+  auto v_tile = [&](int m) { return make_rsrc(vg + (int64_t)m * TK * D, (uint32_t)nd_of(m) * (D * 2)); };
   auto dma = [&](__amdgpu_buffer_rsrc_t rs, lds_char* buf) {
 #pragma unroll
     for (int bi = 0; bi < L::DMA_PER_WAVE; ++bi) L::template dma_block<STREAM>(rs, buf, wave_u, dma_voff, bi);
@@ -1107,13 +1149,44 @@ __device__ __forceinline__ void bf16_fwd_wide(const FwdArgs& a, char* smem_gener
   // Then the DMA wait and the one barrier.
   auto iteration = [&](int j, auto odd_tag, f32x16& s1c, f32x16& s1n, u32x4 (&p0c)[2], u32x4 (&p0n)[2]) {
     constexpr bool odd = decltype(odd_tag)::value;  // j is odd
-    const lds_char* const k_next = odd ? kbuf0 : kbuf1;
-    lds_char* const k_free = odd ? kbuf1 : kbuf0;
-    const lds_char* const v_cur = odd ? vbuf1 : vbuf0;
-    lds_char* const v_free = odd ? vbuf0 : vbuf1;
-    const __amdgpu_buffer_rsrc_t k_rs = k_tile(j + 2), v_rs = v_tile(j + 1);
+    const lds_char* k_next;  // K_{j+1}
+    const lds_char* v_cur;   // V_j
+    // this iteration's DMA: one tile into buffer d0_buf (and, with one 32-key tile per DMA
+    // tile, a second into d1_buf)
+    lds_char* d0_buf;
+    lds_char* d1_buf = nullptr;
+    __amdgpu_buffer_rsrc_t d0_rs, d1_rs;
+    if constexpr (SUB == 1) {
+      k_next = odd ? kbuf0 : kbuf1;
+      v_cur = odd ? vbuf1 : vbuf0;
+      d0_buf = odd ? kbuf1 : kbuf0;  // K_j consumed -> K_{j+2}
+      d1_buf = odd ? vbuf0 : vbuf1;  // V_{j-1} consumed -> V_{j+1}
+      d0_rs = k_tile(j + 2);
+      d1_rs = v_tile(j + 1);
+    } else {
+      // j = 2M or 2M + 1.  K_{j+1} is half (j + 1) & 1 of DMA tile (j + 1) / 2, V_j half j & 1
+      // of DMA tile M.  An even iteration loads V tile M + 1 (into the buffer of V tile M - 1,
+      // last read by iteration 2M - 1), an odd one K tile M + 2 (into that of K tile M, last
+      // read by iteration 2M): each load has two iterations to land.
+      const bool par = ((j >> 1) & 1) != 0;  // parity of M
+      lds_char* const kM = par ? kbuf1 : kbuf0;
+      lds_char* const kM1 = par ? kbuf0 : kbuf1;
+      lds_char* const vM = par ? vbuf1 : vbuf0;
+      lds_char* const vM1 = par ? vbuf0 : vbuf1;
+      if (odd) {
+        k_next = kM1;
+        v_cur = vM + L::HALF_OFF;
+        d0_buf = kM;
+        d0_rs = k_tile((j >> 1) + 2);
+      } else {
+        k_next = kM + L::HALF_OFF;
+        v_cur = vM;
+        d0_buf = vM1;
+        d0_rs = v_tile((j >> 1) + 1);
+      }
+      d1_rs = d0_rs;  // unused
+    }
     const int nv = nv_of(j + 1);
-    constexpr int NF = P::NQ;  // K fragments (and V fragments) per tile: 16
     bf16x8 kf[R], vf[R];
 #pragma unroll
     for (int i = 0; i < R; ++i) kf[i] = P::k_frag(k_next, kbase, 2 * i);
@@ -1128,10 +1201,11 @@ __device__ __forceinline__ void bf16_fwd_wide(const FwdArgs& a, char* smem_gener
         else mfma_vgpr_acc(sg, kf[kk % R], qf[g].v[kk]);
         if (g == 1 && kk + R < NF) kf[kk % R] = P::k_frag(k_next, kbase, 2 * (kk + R));
         if (i >= 2 * NF - R) vf[i - (2 * NF - R)] = P::v_frag(v_cur, vbase, i - (2 * NF - R));
-        if (g == 1) exp_slot(s1c, 1, kk, p1, xe, pe, acc);
-        else if (kk < 2 * L::DMA_PER_WAVE) {
-          if (kk < L::DMA_PER_WAVE) L::template dma_block<STREAM>(k_rs, k_free, wave_u, dma_voff, kk);
-          else L::template dma_block<STREAM>(v_rs, v_free, wave_u, dma_voff, kk - L::DMA_PER_WAVE);
+        if (i % SPE == SPE - 1) exp_slot(s1c, 1, i / SPE, p1, xe, pe, acc);
+        if (g == 0) {
+          if (kk < L::DMA_PER_WAVE) L::template dma_block<STREAM>(d0_rs, d0_buf, wave_u, dma_voff, kk);
+          else if (SUB == 1 && kk < 2 * L::DMA_PER_WAVE)
+            L::template dma_block<STREAM>(d1_rs, d1_buf, wave_u, dma_voff, kk - L::DMA_PER_WAVE);
         }
         __builtin_amdgcn_sched_barrier(0);
       }
@@ -1149,15 +1223,18 @@ __device__ __forceinline__ void bf16_fwd_wide(const FwdArgs& a, char* smem_gener
       float xe[16], pe[16], acc = 0.f;
 #pragma unroll
       for (int i = 0; i < 2 * NF; ++i) {
-        const int vi = i >> 1, g = i & 1;  // V fragment vi: keys 16 (vi / 8) .., columns 32 (vi % 8) ..
-        mfma_agpr_acc(o[g][vi & 7], vf[vi % R], g == 0 ? p0c[vi >> 3] : p1[vi >> 3]);
+        const int vi = i >> 1, g = i & 1;  // V fragment vi: keys 16 (vi / NOB) .., columns 32 (vi % NOB) ..
+        mfma_agpr_acc(o[g][vi % NOB], vf[vi % R], g == 0 ? p0c[vi / NOB] : p1[vi / NOB]);
         if (g == 1 && vi + R < NF) vf[vi % R] = P::v_frag(v_cur, vbase, vi + R);
-        if (g == 1) exp_slot(s0, 0, vi, p0n, xe, pe, acc);
+        if (i % SPE == SPE - 1) exp_slot(s0, 0, i / SPE, p0n, xe, pe, acc);
         __builtin_amdgcn_sched_barrier(0);
       }
       exp_end(s0, 0, acc);
     }
-    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this iteration's tile loads have landed
+    if constexpr (SUB == 1)
+      __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this iteration's tile loads have landed
+    else
+      __builtin_amdgcn_s_waitcnt(0x0F70 | L::DMA_PER_WAVE);  // the previous iteration's tile has landed
     lds_barrier();
   };
 
@@ -1389,12 +1466,12 @@ __device__ __forceinline__ void splitkv_merge_tail(const FwdArgs& a) {
   if (threadIdx.x == 0) a.counters[cidx] = 0;
 }
 
-// 64 query rows per wave at D = 256, bf16 (the host picks it by the wave count, see plan_fwd).
-template <bool PARTIAL, bool STREAM>
+// 64 query rows per wave at D = 256 and 128, bf16 (the host picks it, see plan_fwd).
+template <int D, bool PARTIAL, bool STREAM>
 __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads), amdgpu_waves_per_eu(1, 1)))
 void attn_fwd_wide_kernel(FwdArgs a) {
-  __shared__ __attribute__((aligned(16))) char smem[WideLayout::LDS_BYTES];
-  bf16_fwd_wide<PARTIAL, STREAM>(a, smem);
+  __shared__ __attribute__((aligned(16))) char smem[WideLayout<D>::LDS_BYTES];
+  bf16_fwd_wide<D, PARTIAL, STREAM>(a, smem);
 }
 
 // bf16 D = 256 launches split between the two paths in one grid: workgroups
@@ -1404,9 +1481,9 @@ void attn_fwd_wide_kernel(FwdArgs a) {
 // evenly than either kernel alone (e.g. 2 + 1 rounds instead of 2.5 or 5).
 __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads), amdgpu_waves_per_eu(1, 1)))
 void attn_fwd_mixed_kernel(FwdArgs wide, FwdArgs narrow, int n_wide) {
-  static_assert(WideLayout::LDS_BYTES <= Bf16Dma<256>::LDS_BYTES, "one LDS allocation serves both paths");
+  static_assert(WideLayout<256>::LDS_BYTES <= Bf16Dma<256>::LDS_BYTES, "one LDS allocation serves both paths");
   __shared__ __attribute__((aligned(16))) char smem[Bf16Dma<256>::LDS_BYTES];
-  if ((int)blockIdx.x < n_wide) bf16_fwd_wide<false, false>(wide, smem);
+  if ((int)blockIdx.x < n_wide) bf16_fwd_wide<256, false, false>(wide, smem);
   else bf16_fwd_dma<256, false, false>(narrow, smem);
 }
 

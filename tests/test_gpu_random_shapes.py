@@ -2,8 +2,9 @@
 
 Each case draws B, H, T_q, S, the per-element lengths (0 and S included at
 random), the head dim, the dtype and a scale of either sign, and runs the
-fused forward with each D = 256 path forced (32 or 64 query rows per wave, or
-both in one grid), plus split-KV partials and their merge.
+fused forward with each bf16 path forced (32 or 64 query rows per wave at
+D = 128 and 256, and both in one grid at D = 256), plus split-KV partials and
+their merge.
 """
 
 import math
@@ -44,7 +45,11 @@ def test_random_shape(i, monkeypatch):
     log(f"random case {i}: D={D} {dtype} B={B} H={H} Tq={Tq} S={S} lens={lens} scale={scale:.4f}")
     q, k, v, kv = make_inputs(B, H, Tq, S, D, lens, dtype, 1.0, seed=9100 + i, device=DEV, pad=float("nan"))
     ro, rl = ref_prefix_fwd(to64(q), to64(k), to64(v), np.array(lens), scale)
-    paths = ["128", "256", "mixed"] if (D == 256 and dtype == "bf16") else ["128"]
+    paths = ["128"]
+    if dtype == "bf16" and D == 256:
+        paths = ["128", "256", "mixed"]
+    elif dtype == "bf16" and D == 128:
+        paths = ["128", "256"]
     for rows in paths:
         monkeypatch.setenv("ATTN_PREFIX_FWD_ROWS", rows)
         out, lse = _lib.attn_prefix_fwd(q, k, v, kv, scale)
