@@ -160,7 +160,7 @@ def main() -> int:
     roofline = {
         "bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
         "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": traffic,
-        "kernel": "attn_fwd_wide_kernel<false,false> (64 query rows per wave)", "avg_launch_ms": round(ms_avg, 4),
+        "kernel": "attn_fwd_wide_kernel<256,false,false> (64 query rows per wave)", "avg_launch_ms": round(ms_avg, 4),
         "algorithmic_flop_per_launch": flops,
     }
 
