@@ -272,10 +272,11 @@ def test_no_device_allocation():
 
 
 @pytest.mark.parametrize("D", [64, 256])
-def test_splitkv_other_head_dims(D):
-    B, H, Tq, S = 2, 2, 140, 700
+@pytest.mark.parametrize("Tq", [140, 100])  # 100: one query tile per head (the streaming launch)
+def test_splitkv_other_head_dims(D, Tq):
+    B, H, S = 2, 2, 700
     lens = [650, 0]
-    log(f"splitkv D={D}")
+    log(f"splitkv D={D} Tq={Tq}")
     q, k, v, kv = make_inputs(B, H, Tq, S, D, lens, "bf16", 1.0, seed=1200 + D, device=DEV)
     scale = 1.0 / math.sqrt(D)
     po, pl = _lib.attn_splitkv_partial(q, k, v, kv, 256, scale)
@@ -352,11 +353,14 @@ def test_largest_key_slice(fwd_rows):
 
 
 @pytest.mark.parametrize("D,Tq,chunk,dtype", [(64, 1, 64, "bf16"), (128, 129, 128, "bf16"), (256, 300, 192, "bf16"),
-                                              (128, 200, 64, "f32"), (128, 150, 4096, "bf16")])
+                                              (128, 200, 64, "f32"), (128, 150, 4096, "bf16"), (128, 100, 64, "bf16"),
+                                              (256, 64, 128, "bf16")])
 def test_splitkv_single_launch(D, Tq, chunk, dtype):
     """One launch (partials, then the last chunk per query tile merges) gives the same bits as
     partial + combine, and the oracle's result; partial buffers start as NaN so a merge that
-    read a partial before it was written would show; the counters come back zero."""
+    read a partial before it was written would show; the counters come back zero.  The calls
+    alternate between two query sets, so a merge that read the previous call's partials would
+    show too.  T_q <= 128 takes the streaming launch, whose hand-off is at device scope."""
     B, H, S = 3, 2, 700
     lens = [700, 0, 333]
     log(f"single-launch split D={D} Tq={Tq} chunk={chunk} {dtype}")
@@ -366,17 +370,20 @@ def test_splitkv_single_launch(D, Tq, chunk, dtype):
     po = torch.full((B, H, C, Tq, D), float("nan"), device=DEV)
     pl = torch.full((B, H, C, Tq), float("nan"), device=DEV)
     counters = torch.zeros((B, H, -(-Tq // 128)), dtype=torch.int32, device=DEV)
-    for rep in range(2):  # the second call reuses the counters the first one reset
-        po.fill_(float("nan"))
-        pl.fill_(float("nan"))
-        out, lse = _lib.attn_splitkv_fwd(q, k, v, kv, chunk, scale, part_out=po, part_lse=pl, counters=counters)
+    q_alt = (q.float() * -0.75).to(q.dtype)
+    for rep in range(4):  # later calls reuse the counters the earlier ones reset
+        qq = q if rep % 2 == 0 else q_alt
+        if rep < 2:
+            po.fill_(float("nan"))
+            pl.fill_(float("nan"))
+        out, lse = _lib.attn_splitkv_fwd(qq, k, v, kv, chunk, scale, part_out=po, part_lse=pl, counters=counters)
         torch.cuda.synchronize()
         assert int(counters.abs().sum()) == 0, "counters not reset"
-        rpo, rpl = _lib.attn_splitkv_partial(q, k, v, kv, chunk, scale)
+        rpo, rpl = _lib.attn_splitkv_partial(qq, k, v, kv, chunk, scale)
         rout, rlse = _lib.attn_lse_combine(rpo, rpl, q.dtype)
         torch.cuda.synchronize()
         assert torch.equal(out, rout) and torch.equal(lse, rlse), f"call {rep}: differs from partial + combine"
-    ro, rl = ref_prefix_fwd(to64(q), to64(k), to64(v), np.array(lens), scale)
+    ro, rl = ref_prefix_fwd(to64(qq), to64(k), to64(v), np.array(lens), scale)  # the last call's queries
     assert_parity(out, lse, ro, rl, dtype, f"single-launch split D={D}")
 
 
