@@ -115,7 +115,7 @@ __device__ __forceinline__ void mfma_vgpr_acc(f32x16& d, bf16x8 a, bf16x8 b) {
   asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(d) : "v"(a), "v"(b));
 }
 
-// O^T accumulation for the kernel whose register file is full (64 rows per wave at
+// O^T accumulation for the 64-rows-per-wave kernel (whose register file is full at
 // D = 256): the accumulator is kept in AGPRs and the operands in VGPRs by the constraints,
 // so the compiler cannot move O between register files around the MFMA.  Any VALU read
 // of o (v_accvgpr_read) must leave the XDL wait states.
@@ -866,19 +866,20 @@ __device__ __forceinline__ void bf16_fwd_dma(const FwdArgs& a, char* smem_generi
   }
 }
 
-// ------------------------------------------------ bf16, D = 256, 64 rows per wave
+// ------------------------------------ bf16, D = 256 and 128, 64 rows per wave
 // The same contractions with each wave holding two 32-row groups of queries
 // (64 rows, 256 per workgroup) over 32-key tiles.  Every K operand read and
 // every transposed V read then feeds two MFMAs (one per group), so the LDS
 // operand traffic and the tile DMA per MFMA are half those of bf16_fwd_dma,
 // whose D = 256 form is bound by LDS bandwidth rather than by the MFMA pipe.
-// The register file holds it only just: O of both groups takes all 256 AGPRs,
-// Q of both groups 128 VGPRs.  A 32-key tile is the first 16 blocks of the
-// 64-key layout of Bf16Dma<256> (keys 0..31), so the operand reads and the
-// DMA are those of that layout.  The host takes it for launches whose
-// workgroups fill the GPU's waves better this way (its tiles are twice as
-// tall, so a last, partly filled wave costs more); the rest keep the 32-row
-// kernel.
+// At D = 256 the register file holds it only just: O of both groups takes all
+// 256 AGPRs, Q of both groups 128 VGPRs.  The tiles come from the 64-key layout
+// of Bf16Dma<D> (see WideLayout).  At D = 256 the host takes it for launches
+// whose workgroups fill the GPU's waves better this way (its tiles are twice
+// as tall, so a last, partly filled wave costs more); the rest keep the 32-row
+// kernel.  At D = 128 it is as fast as the 32-row kernel and runs only when
+// forced: with half the MFMAs per 32-key tile, its single wave per SIMD waits on
+// the softmax VALU work.
 constexpr int kBMW = 256;  // query rows per workgroup (64 per wave)
 constexpr int kBNW = 32;   // keys per tile
 
@@ -891,8 +892,9 @@ template <>
 struct WideLayout<256> {
   using P = Bf16Dma<256>;
   static constexpr int SUB = 1;                        // 32-key tiles per DMA tile
+  static constexpr int NBUF = 4;                       // buffers for K, and for V
   static constexpr int TILE_BYTES = 16 * P::BLK;
-  static constexpr int FLAGS = 4 * TILE_BYTES;         // K and V, two buffers each; then 4 flags
+  static constexpr int FLAGS = 2 * NBUF * TILE_BYTES;  // K and V buffers; then 4 flags
   static constexpr int LDS_BYTES = FLAGS + 4 * 4;
   static constexpr int DMA_PER_WAVE = 4;            // 16 blocks per tile over 4 waves
   static constexpr int HALF_OFF = 0;                // unused: one 32-key tile per buffer
@@ -934,8 +936,9 @@ template <>
 struct WideLayout<128> {
   using P = Bf16Dma<128>;
   static constexpr int SUB = 2;
+  static constexpr int NBUF = 2;
   static constexpr int TILE_BYTES = P::TILE_BYTES;
-  static constexpr int FLAGS = 4 * TILE_BYTES;
+  static constexpr int FLAGS = 2 * NBUF * TILE_BYTES;
   static constexpr int LDS_BYTES = FLAGS + 4 * 4;
   static constexpr int DMA_PER_WAVE = P::DMA_PER_WAVE;
   static constexpr int HALF_OFF = 2 * P::ROWB;
@@ -1015,13 +1018,13 @@ __device__ __forceinline__ void bf16_fwd_wide(const FwdArgs& a, char* smem_gener
   constexpr int NOB = D / 32;         // O blocks per group
   constexpr int TK = kBNW * SUB;      // keys per DMA tile
   lds_char* const smem = (lds_char*)smem_generic;
-  lds_char* const kbuf0 = smem;
-  lds_char* const kbuf1 = smem + L::TILE_BYTES;
-  lds_char* const vbuf0 = smem + 2 * L::TILE_BYTES;
-  lds_char* const vbuf1 = smem + 3 * L::TILE_BYTES;
+  // buffer of DMA tile m: K in the first NBUF tile slots, V in the next NBUF
+  static_assert((L::NBUF & (L::NBUF - 1)) == 0, "a power of two buffers");
+  auto kb = [&](int m) { return smem + (m & (L::NBUF - 1)) * L::TILE_BYTES; };
+  auto vb = [&](int m) { return smem + (L::NBUF + (m & (L::NBUF - 1))) * L::TILE_BYTES; };
   volatile __attribute__((address_space(3))) int* const bad_flag =
       (volatile __attribute__((address_space(3))) int*)(smem + L::FLAGS);  // one per wave
-  static_assert(L::FLAGS >= 4 * L::TILE_BYTES && L::FLAGS + 4 * (int)sizeof(int) <= L::LDS_BYTES,
+  static_assert(L::FLAGS >= 2 * L::NBUF * L::TILE_BYTES && L::FLAGS + 4 * (int)sizeof(int) <= L::LDS_BYTES,
                 "the flags sit past the tile buffers, inside the allocation");
 
   const int tid = threadIdx.x;
@@ -1157,22 +1160,27 @@ __device__ __forceinline__ void bf16_fwd_wide(const FwdArgs& a, char* smem_gener
     lds_char* d1_buf = nullptr;
     __amdgpu_buffer_rsrc_t d0_rs, d1_rs;
     if constexpr (SUB == 1) {
-      k_next = odd ? kbuf0 : kbuf1;
-      v_cur = odd ? vbuf1 : vbuf0;
-      d0_buf = odd ? kbuf1 : kbuf0;  // K_j consumed -> K_{j+2}
-      d1_buf = odd ? vbuf0 : vbuf1;  // V_{j-1} consumed -> V_{j+1}
-      d0_rs = k_tile(j + 2);
-      d1_rs = v_tile(j + 1);
+      // four buffers each, and a barrier after odd iterations only: iteration j loads
+      // K_{j+3} and V_{j+2}, into the buffers of K_{j-1} and V_{j-2}, which iteration j - 2
+      // read last (a barrier ends iteration j - 2 or j - 1); the loads of iterations 2p and
+      // 2p + 1 are waited for at the barrier that ends 2p + 1, before iterations 2p + 2 and
+      // 2p + 3 read them
+      k_next = kb(j + 1);
+      v_cur = vb(j);
+      d0_buf = kb(j + 3);
+      d1_buf = vb(j + 2);
+      d0_rs = k_tile(j + 3);
+      d1_rs = v_tile(j + 2);
     } else {
       // j = 2M or 2M + 1.  K_{j+1} is half (j + 1) & 1 of DMA tile (j + 1) / 2, V_j half j & 1
       // of DMA tile M.  An even iteration loads V tile M + 1 (into the buffer of V tile M - 1,
       // last read by iteration 2M - 1), an odd one K tile M + 2 (into that of K tile M, last
       // read by iteration 2M): each load has two iterations to land.
-      const bool par = ((j >> 1) & 1) != 0;  // parity of M
-      lds_char* const kM = par ? kbuf1 : kbuf0;
-      lds_char* const kM1 = par ? kbuf0 : kbuf1;
-      lds_char* const vM = par ? vbuf1 : vbuf0;
-      lds_char* const vM1 = par ? vbuf0 : vbuf1;
+      const int M = j >> 1;
+      lds_char* const kM = kb(M);
+      lds_char* const kM1 = kb(M + 1);
+      lds_char* const vM = vb(M);
+      lds_char* const vM1 = vb(M + 1);
       if (odd) {
         k_next = kM1;
         v_cur = vM + L::HALF_OFF;
@@ -1231,11 +1239,15 @@ __device__ __forceinline__ void bf16_fwd_wide(const FwdArgs& a, char* smem_gener
       }
       exp_end(s0, 0, acc);
     }
-    if constexpr (SUB == 1)
-      __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this iteration's tile loads have landed
-    else
+    if constexpr (SUB == 1) {
+      if constexpr (odd) {
+        __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this pair of iterations' tile loads have landed
+        lds_barrier();
+      }
+    } else {
       __builtin_amdgcn_s_waitcnt(0x0F70 | L::DMA_PER_WAVE);  // the previous iteration's tile has landed
-    lds_barrier();
+      lds_barrier();
+    }
   };
 
   // one pass over the keys; a second runs only if the first marked a row bad (see WideSoftmax)
@@ -1245,15 +1257,19 @@ __device__ __forceinline__ void bf16_fwd_wide(const FwdArgs& a, char* smem_gener
 #pragma unroll
       for (int db = 0; db < D / 32; ++db) o[g][db] = f32x16{};
     sm.l[0] = sm.l[1] = 0.f;
-    dma(k_tile(0), kbuf0);
-    dma(v_tile(0), vbuf0);
-    dma(k_tile(1), kbuf1);
+    dma(k_tile(0), kb(0));
+    dma(v_tile(0), vb(0));
+    dma(k_tile(1), kb(1));
+    if constexpr (SUB == 1) {  // the first pair of iterations reads K_1, K_2, V_0 and V_1
+      dma(k_tile(2), kb(2));
+      dma(v_tile(1), vb(1));
+    }
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's tile loads have landed in LDS
     __syncthreads();
     // S_0 = K_0 Q^T, one K fragment per two MFMAs
 #pragma unroll
     for (int kk = 0; kk < P::NQ; ++kk) {
-      const bf16x8 kf = P::k_frag(kbuf0, kbase, 2 * kk);
+      const bf16x8 kf = P::k_frag(kb(0), kbase, 2 * kk);
       if (kk == 0) {
         mfma_vgpr_first(s0, kf, qf[0].v[0]);
         mfma_vgpr_first(s1a, kf, qf[1].v[0]);
@@ -1481,8 +1497,9 @@ void attn_fwd_wide_kernel(FwdArgs a) {
 // evenly than either kernel alone (e.g. 2 + 1 rounds instead of 2.5 or 5).
 __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads), amdgpu_waves_per_eu(1, 1)))
 void attn_fwd_mixed_kernel(FwdArgs wide, FwdArgs narrow, int n_wide) {
-  static_assert(WideLayout<256>::LDS_BYTES <= Bf16Dma<256>::LDS_BYTES, "one LDS allocation serves both paths");
-  __shared__ __attribute__((aligned(16))) char smem[Bf16Dma<256>::LDS_BYTES];
+  constexpr int kBytes = WideLayout<256>::LDS_BYTES > Bf16Dma<256>::LDS_BYTES ? WideLayout<256>::LDS_BYTES
+                                                                                : Bf16Dma<256>::LDS_BYTES;
+  __shared__ __attribute__((aligned(16))) char smem[kBytes];  // one allocation serves both paths
   if ((int)blockIdx.x < n_wide) bf16_fwd_wide<256, false, false>(wide, smem);
   else bf16_fwd_dma<256, false, false>(narrow, smem);
 }
