@@ -1100,21 +1100,26 @@ __device__ __forceinline__ void bf16_fwd_wide(const FwdArgs& a, char* smem_gener
   // Exponentials of one score block sg (group g) into pk, one element r per call, staged so
   // that no instruction waits on the one just before it: the fma of element r + 2, the exp2
   // of r + 1, then the fp32 sum of r and the bf16 pack of r - 1 and r.
+  // part 0 issues only the fma (in a slot of its own), part 1 the rest, part 2 both.
   auto exp_slot = [&](const f32x16& sg, int g, int r, u32x4 (&pk)[2], float (&xe)[16], float (&pe)[16],
-                      float& acc) {
+                      float& acc, int part) {
     auto fma_of = [&](int k) { return __builtin_fmaf(sg[k], c, -sm.m[g]); };
-    if (r == 0) {
-      xe[0] = fma_of(0);
-      xe[1] = fma_of(1);
-      pe[0] = __builtin_amdgcn_exp2f(xe[0]);
+    if (part != 1) {
+      if (r == 0) {
+        xe[0] = fma_of(0);
+        xe[1] = fma_of(1);
+      }
+      if (r + 2 < 16) xe[r + 2] = fma_of(r + 2);
     }
-    if (r + 2 < 16) xe[r + 2] = fma_of(r + 2);
-    if (r + 1 < 16) pe[r + 1] = __builtin_amdgcn_exp2f(xe[r + 1]);
-    acc += pe[r];
-    if (r & 1) {
-      uint32_t d = pack_bf16x2(pe[r - 1], pe[r]);
-      asm volatile("" : "+v"(d));  // keeps the pack in this slot (it is used only later)
-      pk[r >> 3][(r & 7) >> 1] = d;
+    if (part != 0) {
+      if (r == 0) pe[0] = __builtin_amdgcn_exp2f(xe[0]);
+      if (r + 1 < 16) pe[r + 1] = __builtin_amdgcn_exp2f(xe[r + 1]);
+      acc += pe[r];
+      if (r & 1) {
+        uint32_t d = pack_bf16x2(pe[r - 1], pe[r]);
+        asm volatile("" : "+v"(d));  // keeps the pack in this slot (it is used only later)
+        pk[r >> 3][(r & 7) >> 1] = d;
+      }
     }
   };
   // After a block's exponentials: add the sum to l, and if a lane's sum broke the slack,
@@ -1209,7 +1214,8 @@ __device__ __forceinline__ void bf16_fwd_wide(const FwdArgs& a, char* smem_gener
         else mfma_vgpr_acc(sg, kf[kk % R], qf[g].v[kk]);
         if (g == 1 && kk + R < NF) kf[kk % R] = P::k_frag(k_next, kbase, 2 * (kk + R));
         if (i >= 2 * NF - R) vf[i - (2 * NF - R)] = P::v_frag(v_cur, vbase, i - (2 * NF - R));
-        if (i % SPE == SPE - 1) exp_slot(s1c, 1, i / SPE, p1, xe, pe, acc);
+        // two slots per element: its fma beside the first, the rest beside the second
+        exp_slot(s1c, 1, i / SPE, p1, xe, pe, acc, SPE == 1 ? 2 : i % SPE);
         if (g == 0) {
           if (kk < L::DMA_PER_WAVE) L::template dma_block<STREAM>(d0_rs, d0_buf, wave_u, dma_voff, kk);
           else if (SUB == 1 && kk < 2 * L::DMA_PER_WAVE)
@@ -1234,7 +1240,7 @@ __device__ __forceinline__ void bf16_fwd_wide(const FwdArgs& a, char* smem_gener
         const int vi = i >> 1, g = i & 1;  // V fragment vi: keys 16 (vi / NOB) .., columns 32 (vi % NOB) ..
         mfma_agpr_acc(o[g][vi % NOB], vf[vi % R], g == 0 ? p0c[vi / NOB] : p1[vi / NOB]);
         if (g == 1 && vi + R < NF) vf[vi % R] = P::v_frag(v_cur, vbase, vi + R);
-        if (i % SPE == SPE - 1) exp_slot(s0, 0, i / SPE, p0n, xe, pe, acc);
+        exp_slot(s0, 0, i / SPE, p0n, xe, pe, acc, SPE == 1 ? 2 : i % SPE);
         __builtin_amdgcn_sched_barrier(0);
       }
       exp_end(s0, 0, acc);
@@ -1290,7 +1296,7 @@ __device__ __forceinline__ void bf16_fwd_wide(const FwdArgs& a, char* smem_gener
     {
       float xe[16], pe[16], acc = 0.f;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) exp_slot(s0, 0, r, p0a, xe, pe, acc);
+      for (int r = 0; r < 16; ++r) exp_slot(s0, 0, r, p0a, xe, pe, acc, 2);
       exp_end(s0, 0, acc);
     }
     // iterations 0 .. T2 - 1 with T2 = T rounded up to even: iteration j adds PV_j and takes
