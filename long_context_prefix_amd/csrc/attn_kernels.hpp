@@ -1201,9 +1201,13 @@ __device__ __forceinline__ void bf16_fwd_wide(const FwdArgs& a, char* smem_gener
     }
     const int nv = nv_of(j + 1);
     bf16x8 kf[R], vf[R];
+    // in order, each behind a fence: the first MFMA then waits for the first read only
+    // (the LDS counter counts in issue order)
 #pragma unroll
-    for (int i = 0; i < R; ++i) kf[i] = P::k_frag(k_next, kbase, 2 * i);
-    __builtin_amdgcn_sched_barrier(0);
+    for (int i = 0; i < R; ++i) {
+      kf[i] = P::k_frag(k_next, kbase, 2 * i);
+      __builtin_amdgcn_sched_barrier(0);
+    }
     {
       float xe[16], pe[16], acc = 0.f;
 #pragma unroll
