@@ -323,6 +323,28 @@ def test_growing_scores_exercise_rescale(D):
     assert_parity(out, lse, ro, rl, "bf16", f"growing D={D}")
 
 
+@pytest.mark.parametrize("D", [128, 256])
+def test_score_jump_past_exp_overflow(D, fwd_rows):
+    """One late key block scores more than 128 log2 units above everything before it, so a
+    probability taken against an earlier reference overflows fp32 (2^128): the 32-row kernel
+    must move its max before taking it, the 64-row kernel must redo the pass."""
+    _skip_dup(D, fwd_rows, 300)
+    B, H, Tq, S = 1, 2, 300, 1500
+    q, k, v, kv = make_inputs(B, H, Tq, S, D, [S], "bf16", 1.0, seed=1900 + D, device=DEV)
+    scale = 1.0 / math.sqrt(D)
+    # keys 1200..1263 become a large multiple of the mean query direction
+    qm = q.float().mean(dim=2, keepdim=True)
+    k[:, :, 1200:1264] = (qm / qm.norm(dim=-1, keepdim=True) * 40.0 * math.sqrt(D)).to(torch.bfloat16)
+    s = torch.einsum("bhtd,bhsd->bhts", q.double().cpu(), k.double().cpu()) * scale / math.log(2.0)
+    jump = (s[..., 1200:1264].amax(-1) - s[..., :64].amax(-1)).max().item()
+    assert jump > 128.0, jump
+    log(f"score jump D={D} rows={fwd_rows}: {jump:.0f} log2 units")
+    out, lse = _run_fused(q, k, v, kv, scale)
+    ro, rl = _oracle(q, k, v, kv, scale)
+    assert torch.isfinite(out.float()).all() and torch.isfinite(lse).all()
+    assert_parity(out, lse, ro, rl, "bf16", f"score jump D={D}")
+
+
 @pytest.mark.timeout(900)
 def test_largest_key_slice(fwd_rows):
     """One (b, h) key slice just under the 2^31-byte limit (D=256 bf16, S = 2^22 - 64):
