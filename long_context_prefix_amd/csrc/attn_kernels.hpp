@@ -1100,7 +1100,8 @@ __device__ __forceinline__ void bf16_fwd_wide(const FwdArgs& a, char* smem_gener
   // Exponentials of one score block sg (group g) into pk, one element r per call, staged so
   // that no instruction waits on the one just before it: the fma of element r + 2, the exp2
   // of r + 1, then the fp32 sum of r and the bf16 pack of r - 1 and r.
-  // part 0 issues only the fma (in a slot of its own), part 1 the rest, part 2 both.
+  // part 0 issues the exp2 (a quarter-rate instruction) in a slot of its own, part 1 the
+  // fma, the sum and the pack; part 2 both.
   auto exp_slot = [&](const f32x16& sg, int g, int r, u32x4 (&pk)[2], float (&xe)[16], float (&pe)[16],
                       float& acc, int part) {
     auto fma_of = [&](int k) { return __builtin_fmaf(sg[k], c, -sm.m[g]); };
@@ -1108,12 +1109,12 @@ __device__ __forceinline__ void bf16_fwd_wide(const FwdArgs& a, char* smem_gener
       if (r == 0) {
         xe[0] = fma_of(0);
         xe[1] = fma_of(1);
+        pe[0] = __builtin_amdgcn_exp2f(xe[0]);
       }
-      if (r + 2 < 16) xe[r + 2] = fma_of(r + 2);
+      if (r + 1 < 16) pe[r + 1] = __builtin_amdgcn_exp2f(xe[r + 1]);
     }
     if (part != 0) {
-      if (r == 0) pe[0] = __builtin_amdgcn_exp2f(xe[0]);
-      if (r + 1 < 16) pe[r + 1] = __builtin_amdgcn_exp2f(xe[r + 1]);
+      if (r + 2 < 16) xe[r + 2] = fma_of(r + 2);
       acc += pe[r];
       if (r & 1) {
         uint32_t d = pack_bf16x2(pe[r - 1], pe[r]);
