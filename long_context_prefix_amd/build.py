@@ -2,8 +2,8 @@
 
 Usage: ``python -m long_context_prefix_amd.build`` (or ``build_library()``).
 The device assembly of the same compile is kept in ``_build/`` and checked
-for early reads of inline MFMA results (``isa_check``); a finding fails the
-build.
+for early reads of inline MFMA results and for scratch use by the bf16
+forward kernels (``isa_check``); a finding fails the build.
 """
 
 from __future__ import annotations
@@ -46,7 +46,7 @@ def compile_command(out: str) -> list:
 
 
 def build_library(verbose: bool = False) -> str:
-    from .isa_check import inline_mfma_hazards
+    from .isa_check import inline_mfma_hazards, scratch_findings
 
     tmp = LIB + ".tmp"
     cmd = compile_command(tmp) + ["-save-temps"]
@@ -63,10 +63,15 @@ def build_library(verbose: bool = False) -> str:
         os.makedirs(os.path.dirname(ASM), exist_ok=True)
         shutil.copyfile(asm_files[0], ASM)
     with open(ASM) as f:
-        hazards = inline_mfma_hazards(f.read())
+        text = f.read()
+    hazards = inline_mfma_hazards(text)
     if hazards:
         os.remove(tmp)
         raise RuntimeError("inline MFMA result read too early:\n" + "\n".join(hazards[:10]))
+    spills = scratch_findings(text)
+    if spills:
+        os.remove(tmp)
+        raise RuntimeError("forward kernels use scratch memory:\n" + "\n".join(spills[:10]))
     os.replace(tmp, LIB)
     return LIB
 

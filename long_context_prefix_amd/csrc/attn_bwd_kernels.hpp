@@ -40,6 +40,7 @@ struct BwdArgs {
   float scale;
   float scale_log2;  // scale * log2(e)
   int n_tiles;       // grid decode: query tiles (dq) or key blocks (dkdv) per (b, h)
+  int order_b;       // 1: batch elements are walked longest prefix first (1 < B <= 64)
   void* dq;
   void* dk;
   void* dv;
@@ -124,7 +125,7 @@ void bwd_dq_slot_kernel(BwdArgs a) {
   int wg = blockIdx.x;
   const int qt = wg % a.n_tiles;
   wg /= a.n_tiles;
-  const int h = wg % a.H, b = wg / a.H;
+  const int h = wg % a.H, b = a.order_b ? longest_first(a.kv_len, a.B, a.S, wg / a.H) : wg / a.H;
   int n = a.kv_len[b];
   n = n < 0 ? 0 : (n > a.S ? a.S : n);
   const int64_t bh = (int64_t)b * a.H + h;
@@ -288,7 +289,7 @@ void bwd_dkdv_slot_kernel(BwdArgs a) {
   int wg = blockIdx.x;
   const int kblk = wg % a.n_tiles;
   wg /= a.n_tiles;
-  const int h = wg % a.H, b = wg / a.H;
+  const int h = wg % a.H, b = a.order_b ? longest_first(a.kv_len, a.B, a.S, wg / a.H) : wg / a.H;
   int n = a.kv_len[b];
   n = n < 0 ? 0 : (n > a.S ? a.S : n);
   const int64_t bh = (int64_t)b * a.H + h;
@@ -504,7 +505,7 @@ void bwd_dkdv_pipe_kernel(BwdArgs a) {
   int wg = blockIdx.x;
   const int kblk = wg % a.n_tiles;
   wg /= a.n_tiles;
-  const int h = wg % a.H, b = wg / a.H;
+  const int h = wg % a.H, b = a.order_b ? longest_first(a.kv_len, a.B, a.S, wg / a.H) : wg / a.H;
   int n = a.kv_len[b];
   n = n < 0 ? 0 : (n > a.S ? a.S : n);
   const int64_t bh = (int64_t)b * a.H + h;

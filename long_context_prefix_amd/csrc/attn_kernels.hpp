@@ -67,6 +67,7 @@ struct FwdArgs {
   int32_t* counters; // single-launch split mode: [B,H,n_qtiles] arrival counts, zero between launches
   int wg_base;        // workgroups of this part start at blockIdx.x = wg_base (a launch split
   int row_base;       // between two kernels' paths); its query rows start at row_base
+  int order_b;        // 1: batch elements are walked longest prefix first (1 < B <= 64)
 };
 
 __device__ __forceinline__ float pair_max(float x) {
@@ -396,9 +397,35 @@ struct F32Path {
 };
 
 // ------------------------------------------------------------ the fwd kernels
+// Batch element with the r-th longest prefix (equal lengths in index order), for
+// 1 < B <= 64, from the device-resident lengths and without a host round trip.
+// Packed batches have a different boundary per element (tabfm PR #80, section
+// Fix), so workgroups of a long element run for longer: walking the elements
+// longest first leaves the short ones for the end of the launch, where they fill
+// the gaps instead of one long element running alone.  Lane i < B takes n_i and
+// counts the elements ordered before it; the lane whose count is r names the
+// element.  The result is wave-uniform.
+__device__ __forceinline__ int longest_first(const int32_t* kv_len, int B, int S, int r) {
+  const int lane = (int)(threadIdx.x & 63);
+  int ni = -1;
+  if (lane < B) {
+    ni = kv_len[lane];
+    ni = ni < 0 ? 0 : (ni > S ? S : ni);
+  }
+  int rank = 0;
+  for (int j = 0; j < B; ++j) {
+    const int nj = __builtin_amdgcn_readlane(ni, j);
+    rank += (nj > ni || (nj == ni && j < lane)) ? 1 : 0;
+  }
+  const uint64_t hit = __builtin_amdgcn_ballot_w64(lane < B && rank == r);
+  return __builtin_amdgcn_readfirstlane((int)__builtin_ctzll(hit));
+}
+constexpr int kMaxOrderedBatch = 64;
+
 // Workgroup id -> (query tile, [chunk], head, batch), query tile fastest, so
 // the workgroups resident at one time walk the same (b, h) key stream and
-// share it through L2.
+// share it through L2.  The batch index is the slowest, in longest-first order
+// when order_b is set.
 struct Work {
   int b, h, c, lo, hi, row;
   bool row_ok;
@@ -418,7 +445,7 @@ __device__ __forceinline__ Work decode(const FwdArgs& a, int tile_rows, int loca
     wg /= a.C;
   }
   w.h = wg % a.H;
-  w.b = wg / a.H;
+  w.b = a.order_b ? longest_first(a.kv_len, a.B, a.S, wg / a.H) : wg / a.H;
   int n = a.kv_len[w.b];
   n = n < 0 ? 0 : (n > a.S ? a.S : n);  // out-of-range lengths are clamped, never trusted
   w.lo = 0;
@@ -498,6 +525,43 @@ __device__ __forceinline__ void write_partial_staged(const FwdArgs& a, const Wor
     __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, x), rs, (uint32_t)(idx * 16), 0, kCpolSc1Nt);
   }
   if (h_half == 0 && w.row_ok) a.part_lse[w.out_row] = lse_nat;
+}
+
+// The bf16 output rows of one 32-row group through LDS, as write_partial_staged does for
+// the fp32 partials: lane (r, h) holds 8 bytes of each 16-byte unit 4 db + rg of row r
+// (columns 32 db + 8 rg + 4 h ..), staged row-major with unit u of row r at u ^ (r mod D/8);
+// then each store instruction writes 1 KB of consecutive rows (2, 4 or 8 whole rows), at
+// device scope and non-temporal, instead of 8-byte pieces of 32 rows.  The 8-byte pieces
+// cost 2.6 times the output bytes in HBM writes at the 121k-key ICL shape.
+template <int D>
+__device__ __forceinline__ void write_out_staged(const FwdArgs& a, const Work& w, const f32x16 (&o)[D / 32],
+                                                 float inv_l, float lse_nat, int h_half, lds_char* stage, int lane) {
+  constexpr int U = D / 8;  // 16-byte units per row
+  const int r = lane & 31;
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+    for (int rg = 0; rg < 4; ++rg) {
+      const int u = 4 * db + rg;
+      const u32x2 x = {pack_bf16x2(o[db][4 * rg + 0] * inv_l, o[db][4 * rg + 1] * inv_l),
+                       pack_bf16x2(o[db][4 * rg + 2] * inv_l, o[db][4 * rg + 3] * inv_l)};
+      *reinterpret_cast<__attribute__((address_space(3))) u32x2*>(stage + (r * U + (u ^ (r & (U - 1)))) * 16 +
+                                                                  8 * h_half) = x;
+    }
+  // the group's rows [row0, row0 + 32) are consecutive rows of out; rows at or past Tq lie
+  // outside the resource, so their stores are dropped
+  const int row0 = w.row - r;
+  const int nrows = min(max(a.Tq - row0, 0), 32);
+  const __amdgpu_buffer_rsrc_t rs =
+      make_rsrc(reinterpret_cast<uint16_t*>(a.out) + (w.out_row - r) * D, (uint32_t)(nrows * D * 2));
+#pragma unroll
+  for (int k = 0; k < 32 * U / 64; ++k) {
+    const int idx = 64 * k + lane, rr = idx / U, c = idx % U;
+    const u32x4 x = *reinterpret_cast<const __attribute__((address_space(3))) u32x4*>(
+        stage + (rr * U + (c ^ (rr & (U - 1)))) * 16);
+    __builtin_amdgcn_raw_buffer_store_b128(x, rs, (uint32_t)(idx * 16), 0, kCpolSc1Nt);
+  }
+  if (h_half == 0 && w.row_ok && a.lse) a.lse[w.out_row] = lse_nat;
 }
 
 template <class P, int D, bool PARTIAL>
@@ -631,29 +695,6 @@ struct Softmax {
         for (int r = 0; r < 16; ++r) o[db][r] *= alpha;
     }
   }
-
-  // p = 2^(c*s - m), rounded to bf16 pairs in S^T register order; masked keys give p = 0.
-  template <bool MASK>
-  __device__ __forceinline__ void exp_pack(const f32x16 (&s)[kBN / 32], float c, u32x4 (&pk)[kBN / 16], int nv,
-                                           int h_half) {
-    const float nm = -m;
-    float acc[4] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int ks = 0; ks < kBN / 16; ++ks) {
-      float p[8];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int r = 8 * (ks & 1) + e;
-        float x = __builtin_amdgcn_exp2f(__builtin_fmaf(s[ks >> 1][r], c, nm));
-        if (MASK && st_key(ks >> 1, r, h_half) >= nv) x = 0.0f;
-        p[e] = x;
-        acc[e & 3] += x;
-      }
-      pk[ks] = u32x4{pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]), pack_bf16x2(p[4], p[5]),
-                     pack_bf16x2(p[6], p[7])};
-    }
-    l += (acc[0] + acc[1]) + (acc[2] + acc[3]);
-  }
 };
 
 
@@ -663,8 +704,14 @@ struct Softmax {
 // buffers the previous iteration released, issues S_{j+1} = K_{j+1} Q^T on the
 // MFMA pipe while the exponentials of tile j run on the VALU, accumulates
 // O += V_j P_j while the VALU takes the row max of S_{j+1}, then waits for its
-// DMA and meets the other waves at the one barrier of the iteration.  The last
-// tile, whose keys may be masked, takes its max after the loop.
+// DMA and meets the other waves at the one barrier of the iteration.  Scores of a
+// tile that holds keys at or past the end are masked to -inf (a rare branch) before
+// its max is taken.  The loop runs an even number of iterations, so the last one or
+// two take phantom tiles past the end: their DMA zero-fills LDS without a memory
+// request and every score is masked, so they add p = 0.  The PV product of the last
+// real tile then needs no code of its own (a separate last-tile path made the
+// register allocator spill), and the loop body is one pair of iterations whose score
+// register sets alternate without copies.
 //
 // The iteration is written as fixed slots -- one MFMA, the LDS operand read
 // for the MFMA kRing slots later, a share of the softmax work and, in the
@@ -672,6 +719,11 @@ struct Softmax {
 // fences that keep the compiler from regrouping them.  At D = 256 (one wave
 // per SIMD) nothing else hides a stall; at D = 128 and 64 (two waves per SIMD)
 // the fixed order still measured 4-4.5% faster than the compiler's.
+// Marks a branch whose body runs rarely (the last tile's mask, the slack check's max): an
+// empty volatile asm cannot be executed speculatively, so the compiler keeps the branch
+// instead of turning its body into selects computed on every iteration.
+__device__ __forceinline__ void rare_path() { asm volatile(""); }
+
 constexpr int kRing = 2;  // LDS operand reads issued this many slots ahead (2..4 measure the same)
 
 template <int D, bool PARTIAL, bool STREAM>
@@ -716,8 +768,23 @@ __device__ __forceinline__ void bf16_fwd_dma(const FwdArgs& a, char* smem_generi
       qf.v[kk] = __builtin_bit_cast(bf16x8, x);
     }
   }
+  // masked keys are -inf scores, and c * -inf must stay -inf: a zero scale is taken as the
+  // smallest normal float (every finite score then gives 2^0 = 1 to within fp32 rounding)
+  c = fmaxf(c, 1.17549435e-38f);
   const int kbase = P::k_base(lane);
   const int vbase = P::v_base(lane);
+  // keys at or past nv of a tile get s = -inf; the key indices come from an opaque copy of
+  // the lane's half, so that they are computed in the rare branch instead of being hoisted
+  // out of the tile loop into live registers
+  auto mask_scores = [&](f32x16 (&sg)[kBN / 32], int nv) {
+    int hh = h_half;
+    asm volatile("" : "+v"(hh));
+#pragma unroll
+    for (int kb = 0; kb < kBN / 32; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+        if (st_key(kb, r, hh) >= nv) sg[kb][r] = -__builtin_inff();
+  };
 
   P::template dma_tile<STREAM>(k_tile(0), kbuf0, wave_u, lane);
   P::template dma_tile<STREAM>(v_tile(0), vbuf0, wave_u, lane);
@@ -742,12 +809,12 @@ __device__ __forceinline__ void bf16_fwd_dma(const FwdArgs& a, char* smem_generi
   for (int db = 0; db < D / 32; ++db) o[db] = f32x16{};
   Softmax<D> sm;
   u32x4 pk[kBN / 16];
-  if (T >= 2) sm.apply_max(Softmax<D>::row_max(s_cur, c), o);  // tile 0 is full when more follow
+  if (nv_of(0) < kBN) mask_scores(s_cur, nv_of(0));
+  sm.apply_max(Softmax<D>::row_max(s_cur, c), o);
 
   // sc holds S_j; S_{j+1} is accumulated into sn (two register sets, used alternately, so that
   // no MFMA of one iteration has to wait for the reads of the previous iteration's scores)
-  auto iteration = [&](int j, auto next_max_tag, f32x16 (&sc)[kBN / 32], f32x16 (&sn)[kBN / 32]) {
-    constexpr bool NEXT_MAX = decltype(next_max_tag)::value;  // take S_{j+1}'s max here
+  auto iteration = [&](int j, f32x16 (&sc)[kBN / 32], f32x16 (&sn)[kBN / 32]) {
     lds_char* const k_next = (j & 1) ? kbuf0 : kbuf1;  // K_{j+1}
     lds_char* const k_free = (j & 1) ? kbuf1 : kbuf0;  // K_j consumed -> K_{j+2}
     lds_char* const v_cur = (j & 1) ? vbuf1 : vbuf0;   // V_j
@@ -803,57 +870,39 @@ __device__ __forceinline__ void bf16_fwd_dma(const FwdArgs& a, char* smem_generi
       // on top of the two MFMA issues in between)
       asm volatile("s_nop 7\n\ts_nop 7" ::: "memory");
       __builtin_amdgcn_sched_barrier(0);
+      if (nv_of(j + 1) < kBN) {
+        rare_path();
+        mask_scores(sn, nv_of(j + 1));
+      }
+      __builtin_amdgcn_sched_barrier(0);
       float mx = -__builtin_inff();
 #pragma unroll
       for (int i = 0; i < NV; ++i) {
         const int ks = i / (D / 32), db = i % (D / 32);
         o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[i % R], __builtin_bit_cast(bf16x8, pk[ks]), o[db], 0, 0, 0);
         if (i + R < NV) vf[i % R] = P::v_frag(v_cur, vbase, i + R);
-        if constexpr (NEXT_MAX) {
 #pragma unroll
-          for (int t = 0; t < MPS; ++t) {
-            const int e = i * MPS + t;
-            mx = fmaxf(mx, sn[e >> 4][e & 15]);
-          }
+        for (int t = 0; t < MPS; ++t) {
+          const int e = i * MPS + t;
+          mx = fmaxf(mx, sn[e >> 4][e & 15]);
         }
         __builtin_amdgcn_sched_barrier(0);
       }
-      if constexpr (NEXT_MAX) sm.apply_max(pair_max(mx) * c, o);
+      sm.apply_max(pair_max(mx) * c, o);
     }
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this iteration's tile loads have landed
     lds_barrier();
   };
 
+  // iterations 0 .. T2 - 1, T2 = T rounded up to even: iteration j adds PV_j and takes the
+  // scores of tile j + 1 (phantom tiles at or past T are all masked)
   f32x16 s_alt[kBN / 32];
-  {  // unrolled by two so that the score register sets alternate without copies
-    int j = 0;
-    for (; j + 1 < T - 2; j += 2) {
-      iteration(j, std::true_type{}, s_cur, s_alt);
-      iteration(j + 1, std::true_type{}, s_alt, s_cur);
-    }
-    if (j < T - 2) {  // one more full iteration, then the last one
-      iteration(j, std::true_type{}, s_cur, s_alt);
-      iteration(j + 1, std::false_type{}, s_alt, s_cur);
-    } else if (T >= 2) {
-      iteration(T - 2, std::false_type{}, s_cur, s_alt);
-#pragma unroll
-      for (int kb = 0; kb < kBN / 32; ++kb) s_cur[kb] = s_alt[kb];
-    }
+  const int T2 = (T + 1) & ~1;
+  for (int j = 0; j < T2; j += 2) {
+    iteration(j, s_cur, s_alt);
+    iteration(j + 1, s_alt, s_cur);
   }
   __builtin_amdgcn_s_waitcnt(0x0F70);  // no tile load may still be writing LDS when the workgroup ends
-
-  // last tile: S_{T-1} in s_cur, V_{T-1} in vbuf[(T-1) & 1]; keys >= nv are masked
-  const int nv_last = nv_of(T - 1);
-  if (nv_last < kBN) {
-#pragma unroll
-    for (int kb = 0; kb < kBN / 32; ++kb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r)
-        if (st_key(kb, r, h_half) >= nv_last) s_cur[kb][r] = -__builtin_inff();
-  }
-  sm.apply_max(Softmax<D>::row_max(s_cur, c), o);
-  sm.template exp_pack<true>(s_cur, c, pk, nv_last, h_half);
-  P::accumulate(o, pk, ((T - 1) & 1) ? vbuf1 : vbuf0, vbase);
 
   const float l = pair_sum(sm.l);
   if constexpr (PARTIAL && STREAM) {
@@ -861,6 +910,11 @@ __device__ __forceinline__ void bf16_fwd_dma(const FwdArgs& a, char* smem_generi
     lds_barrier();  // every wave is done with the last V tile: the buffers take the partial rows
     write_partial_staged<D>(a, w, o, 1.0f / l, (sm.m + __builtin_amdgcn_logf(l)) * kLn2, h_half,
                             smem + wave * (32 * D * 4), lane);
+  } else if constexpr (!PARTIAL) {
+    static_assert(4 * 32 * D * 2 <= P::LDS_BYTES, "four waves' output rows fit the tile buffers");
+    lds_barrier();  // every wave is done with the last V tile: the buffers take the output rows
+    write_out_staged<D>(a, w, o, 1.0f / l, (sm.m + __builtin_amdgcn_logf(l)) * kLn2, h_half,
+                        smem + wave * (32 * D * 2), lane);
   } else {
     write_rows<P, D, PARTIAL>(a, w, o, 1.0f / l, (sm.m + __builtin_amdgcn_logf(l)) * kLn2, h_half);
   }
@@ -980,11 +1034,6 @@ __device__ __forceinline__ void s_result_guard(f32x16& s0, f32x16& s1) {
   asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+v"(s0), "+v"(s1));
   __builtin_amdgcn_sched_barrier(0);
 }
-
-// Marks a branch whose body runs rarely (the last tile's mask, the slack check's max): an
-// empty volatile asm cannot be executed speculatively, so the compiler keeps the branch
-// instead of turning its body into selects computed on every iteration.
-__device__ __forceinline__ void rare_path() { asm volatile(""); }
 
 // Softmax state of one lane of the 64-row kernel: its two rows (groups 0 and 1).
 //
@@ -1332,12 +1381,20 @@ __device__ __forceinline__ void bf16_fwd_wide(const FwdArgs& a, char* smem_gener
   Work we[2];
   we[0] = decode<PARTIAL>(a, kBMW, (tid_e >> 6) * 64 + (tid_e & 31));
   we[1] = next_group(a, we[0]);
+  // every wave is past the barriers that end the pass, so the tile buffers are free: the
+  // output rows of group g of wave w are staged in region 2 w + g
+  static_assert(8 * 32 * D * 2 <= L::FLAGS, "eight groups' output rows fit the tile buffers");
 #pragma unroll
   for (int g = 0; g < 2; ++g) {
 #pragma unroll
     for (int db = 0; db < D / 32; ++db) o_result_guard(o[g][db]);  // the epilogue reads O
     const float l = pair_sum(sm.l[g]);
-    write_rows<P, D, PARTIAL>(a, we[g], o[g], 1.0f / l, (sm.m[g] + __builtin_amdgcn_logf(l)) * kLn2, (tid_e >> 5) & 1);
+    const float lse_nat = (sm.m[g] + __builtin_amdgcn_logf(l)) * kLn2;
+    if constexpr (PARTIAL)
+      write_rows<P, D, PARTIAL>(a, we[g], o[g], 1.0f / l, lse_nat, (tid_e >> 5) & 1);
+    else
+      write_out_staged<D>(a, we[g], o[g], 1.0f / l, lse_nat, (tid_e >> 5) & 1,
+                          smem + (2 * (tid_e >> 6) + g) * (32 * D * 2), tid_e & 63);
   }
 }
 
@@ -1469,7 +1526,7 @@ __device__ __forceinline__ void splitkv_merge_tail(const FwdArgs& a) {
   const int qt = wg % a.n_qtiles;
   wg /= a.n_qtiles;
   wg /= a.C;
-  const int h = wg % a.H, b = wg / a.H;
+  const int h = wg % a.H, b = a.order_b ? longest_first(a.kv_len, a.B, a.S, wg / a.H) : wg / a.H;
   const int64_t bh = (int64_t)b * a.H + h;
   const int64_t cidx = bh * a.n_qtiles + qt;
   __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this thread's partial stores have reached L2

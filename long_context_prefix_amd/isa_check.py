@@ -124,3 +124,35 @@ def inline_mfma_hazards(asm: str, wait_states: int = WAIT_STATES) -> List[str]:
             elif writes & dst:
                 found.append(f"{kernel}: '{u}' overwrites the result of '{t}' after {ws} wait states")
     return found
+
+
+# Kernels whose registers must fit without scratch: every bf16 forward and split-KV partial
+# kernel (32- and 64-row, fused, partial, merging, mixed).  A spill there moves bytes through
+# memory on every launch (at the inducing split-KV shape two 16-byte spills per lane were
+# 131 MB of scratch writes per launch).  The fp32 path, kept for correctness only, and the
+# backward kernels are not covered.
+_NO_SCRATCH = re.compile(r"^_ZN3lcp(15attn_fwd_kernelINS_7Bf16Dma|20attn_fwd_wide_kernel|21attn_fwd_mixed_kernel)")
+_KERNEL_DESC = re.compile(r"^\s*\.amdhsa_kernel\s+(\S+)")
+_PRIVATE = re.compile(r"^\s*\.amdhsa_private_segment_fixed_size\s+(\d+)")
+
+
+def private_segment_sizes(asm: str) -> dict:
+    """Per-lane scratch bytes of every kernel descriptor in the assembly."""
+    sizes = {}
+    kernel = None
+    for line in asm.split("\n"):
+        m = _KERNEL_DESC.match(line)
+        if m:
+            kernel = m.group(1)
+            continue
+        m = _PRIVATE.match(line)
+        if m and kernel is not None:
+            sizes[kernel] = int(m.group(1))
+            kernel = None
+    return sizes
+
+
+def scratch_findings(asm: str) -> List[str]:
+    """The forward kernels that must not use scratch but do."""
+    return [f"{k}: {n} bytes of scratch per lane" for k, n in sorted(private_segment_sizes(asm).items())
+            if n > 0 and _NO_SCRATCH.match(k)]

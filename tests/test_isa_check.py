@@ -84,3 +84,33 @@ def test_operand_written_just_before_an_inline_mfma_is_found():
     assert inline_mfma_hazards(asm) == []
     # an unrelated write is fine
     assert inline_mfma_hazards(_asm_a(before=("v_cvt_pk_bf16_f32 v70, v40, v41",))) == []
+
+
+def test_scratch_use_of_forward_kernels_is_found():
+    from long_context_prefix_amd.isa_check import private_segment_sizes, scratch_findings
+
+    def desc(name, n):
+        return f"\t.amdhsa_kernel {name}\n\t\t.amdhsa_group_segment_fixed_size 0\n" \
+               f"\t\t.amdhsa_private_segment_fixed_size {n}\n\t.end_amdhsa_kernel\n"
+
+    fwd = "_ZN3lcp15attn_fwd_kernelINS_7Bf16DmaILi128EEELi128ELb1ELi2ELb1ELb0EEEvNS_7FwdArgsE"
+    wide = "_ZN3lcp20attn_fwd_wide_kernelILi256ELb0ELb0EEEvNS_7FwdArgsE"
+    f32 = "_ZN3lcp15attn_fwd_kernelINS_7F32PathILi256EEELi256ELb0ELi1ELb0ELb0EEEvNS_7FwdArgsE"
+    bwd = "_ZN3lcp20bwd_dkdv_slot_kernelILi256ELi1EEEvNS_7BwdArgsE"
+    asm = desc(fwd, 36) + desc(wide, 0) + desc(f32, 844) + desc(bwd, 8)
+    assert private_segment_sizes(asm) == {fwd: 36, wide: 0, f32: 844, bwd: 8}
+    found = scratch_findings(asm)
+    assert len(found) == 1 and fwd in found[0]  # the fp32 path and the backward are not covered
+    assert scratch_findings(desc(fwd, 0) + desc(wide, 0)) == []
+    assert len(scratch_findings(desc(wide, 4))) == 1
+
+
+def test_built_forward_kernels_use_no_scratch():
+    from long_context_prefix_amd.isa_check import private_segment_sizes, scratch_findings
+
+    if not os.path.exists(build.ASM):
+        pytest.skip("library not built here")
+    text = open(build.ASM).read()
+    sizes = private_segment_sizes(text)
+    assert any("Bf16DmaILi128" in k for k in sizes)  # the D = 128 forward kernels are in the build
+    assert scratch_findings(text) == []
