@@ -46,8 +46,13 @@
  * returns ATTN_ERR_HIP.
  *
  * Limits.  D in {64, 128, 256}; dtype bf16 or fp32 (inputs and `out` share
- * it); S * D * sizeof(dtype) < 2^31 per (b, h); the number of workgroups
- * (B * H * ceil(Tq / 128) [* C]) below 2^31.  Zero B, H or Tq is a no-op
+ * it); S * D * sizeof(dtype) < 2^31 per (b, h); every launch within the 32-bit
+ * work-item count of a 1-D dispatch: B * H * ceil(Tq / 128) [* C] workgroups
+ * of 256 threads at most 2^24 - 1 for the forward and split calls (the same
+ * bound on ceil(B*H*Tq*D / 1024) for the merge, and on ceil(B*H*Tq*D / 2048),
+ * B * H * ceil(Tq / 128) and B * H * ceil(S / 128) for the backward; B at most
+ * 2^23 - 1 rows for the mask call).  Larger calls return ATTN_ERR_SHAPE before
+ * any launch; size checks come before pointer checks.  Zero B, H or Tq is a no-op
  * returning ATTN_OK (then the tensor pointers may be NULL); S = 0 is legal
  * (every n_b is 0) and then k and v may be NULL.
  */

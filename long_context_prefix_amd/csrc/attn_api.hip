@@ -18,6 +18,10 @@ using namespace lcp;
 namespace {
 
 constexpr int64_t kMaxI32 = 2147483647;
+// A 1-D dispatch counts work-items (workgroups x threads) in 32 bits, so a launch of wgs
+// workgroups of `threads` threads fits only while wgs * threads < 2^32.
+constexpr int64_t kMaxWorkItems = 4294967295LL;
+bool grid_fits(int64_t wgs, int threads) { return wgs >= 0 && wgs <= kMaxWorkItems / threads; }
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
@@ -52,15 +56,16 @@ attn_status_t check_fwd(const void* q, const void* k, const void* v, const int32
     *noop = true;
     return ATTN_OK;
   }
-  if (!q || !kv_len || !out || (out2_required && !out2)) return ATTN_ERR_NULLPTR;
-  if (S > 0 && (!k || !v)) return ATTN_ERR_NULLPTR;
-  if (!aligned16(q) || !aligned16(out) || (out2 && !aligned4(out2)) || !aligned4(kv_len)) return ATTN_ERR_ALIGN;
-  if (S > 0 && (!aligned16(k) || !aligned16(v))) return ATTN_ERR_ALIGN;
+  // sizes before pointers
   if ((int64_t)S * D * esize(dtype) > kMaxI32) return ATTN_ERR_SHAPE;
   const int64_t nqt = ((int64_t)Tq + kBM - 1) / kBM;
   int64_t grid = nqt * B * H;
   if (split) grid *= ((int64_t)S + chunk_or_zero - 1) / chunk_or_zero;
-  if (grid > kMaxI32) return ATTN_ERR_SHAPE;
+  if (!grid_fits(grid, kThreads)) return ATTN_ERR_SHAPE;
+  if (!q || !kv_len || !out || (out2_required && !out2)) return ATTN_ERR_NULLPTR;
+  if (S > 0 && (!k || !v)) return ATTN_ERR_NULLPTR;
+  if (!aligned16(q) || !aligned16(out) || (out2 && !aligned4(out2)) || !aligned4(kv_len)) return ATTN_ERR_ALIGN;
+  if (S > 0 && (!aligned16(k) || !aligned16(v))) return ATTN_ERR_ALIGN;
   return ATTN_OK;
 }
 
@@ -234,6 +239,7 @@ attn_status_t attn_prefix_mask_to_kv_len(const uint8_t* mask, int B, int S, int6
                                          void* stream) {
   if (B < 0 || S < 0 || row_stride < 0) return ATTN_ERR_SHAPE;
   if (B == 0) return ATTN_OK;
+  if (!grid_fits(B, kMaskThreads)) return ATTN_ERR_SHAPE;
   if (!kv_len || (S > 0 && !mask)) return ATTN_ERR_NULLPTR;
   if (!aligned4(kv_len)) return ATTN_ERR_ALIGN;
   if (verbose()) fprintf(stderr, "[attn_prefix] prefix_mask_to_kv_len B=%d S=%d\n", B, S);
@@ -251,6 +257,14 @@ attn_status_t attn_prefix_bwd(const void* q, const void* k, const void* v, const
   if (dtype != ATTN_BF16 || (D != 64 && D != 128 && D != 256)) return ATTN_ERR_UNSUPPORTED;
   if (!isfinite(scale)) return ATTN_ERR_ARG;
   if (B == 0 || H == 0 || (Tq == 0 && S == 0)) return ATTN_OK;
+  // sizes before pointers
+  if ((int64_t)S * D * 2 > kMaxI32) return ATTN_ERR_SHAPE;
+  const int64_t rows = (int64_t)B * H * Tq;
+  const int64_t grid_dq = (int64_t)B * H * ((Tq + kBM - 1) / kBM);
+  const int64_t grid_dkdv = (int64_t)B * H * (((int64_t)S + 127) / 128);
+  const int64_t grid_delta = (rows + 256 / (D / 8) - 1) / (256 / (D / 8));
+  if (!grid_fits(grid_dq, kThreads) || !grid_fits(grid_dkdv, kThreads) || !grid_fits(grid_delta, 256))
+    return ATTN_ERR_SHAPE;
   if (!kv_len) return ATTN_ERR_NULLPTR;
   if (Tq > 0 && (!q || !out || !dout || !lse || !delta || !dq)) return ATTN_ERR_NULLPTR;
   if (S > 0 && (!dk || !dv)) return ATTN_ERR_NULLPTR;
@@ -261,11 +275,6 @@ attn_status_t attn_prefix_bwd(const void* q, const void* k, const void* v, const
     return ATTN_ERR_ALIGN;
   if (S > 0 && (!aligned16(dk) || !aligned16(dv) || (Tq > 0 && (!aligned16(k) || !aligned16(v)))))
     return ATTN_ERR_ALIGN;
-  if ((int64_t)S * D * 2 > kMaxI32) return ATTN_ERR_SHAPE;
-  const int64_t rows = (int64_t)B * H * Tq;
-  const int64_t grid_dq = (int64_t)B * H * ((Tq + kBM - 1) / kBM);
-  const int64_t grid_dkdv = (int64_t)B * H * (((int64_t)S + 127) / 128);
-  if (grid_dq > kMaxI32 || grid_dkdv > kMaxI32 || rows / (256 / (D / 8)) >= kMaxI32) return ATTN_ERR_SHAPE;
   BwdArgs a{};
   a.q = q;
   a.k = k;
@@ -281,6 +290,7 @@ attn_status_t attn_prefix_bwd(const void* q, const void* k, const void* v, const
   a.S = S;
   a.scale = scale;
   a.scale_log2 = scale * kLog2e;
+  a.order_b = (B > 1 && B <= kMaxOrderedBatch) ? 1 : 0;
   a.dq = dq;
   a.dk = dk;
   a.dv = dv;
@@ -333,6 +343,7 @@ attn_status_t attn_prefix_fwd(const void* q, const void* k, const void* v, const
   a.chunk = 0;
   a.C = 1;
   a.n_qtiles = (Tq + kBM - 1) / kBM;
+  a.order_b = (B > 1 && B <= kMaxOrderedBatch) ? 1 : 0;
   a.out = out;
   a.lse = lse;
   const FwdPlan plan = plan_fwd(D, dtype, B, H, Tq);
@@ -366,6 +377,7 @@ attn_status_t attn_splitkv_partial(const void* q, const void* k, const void* v, 
   a.chunk = chunk;
   a.C = C;
   a.n_qtiles = (Tq + kBM - 1) / kBM;
+  a.order_b = (B > 1 && B <= kMaxOrderedBatch) ? 1 : 0;
   a.part_out = part_out;
   a.part_lse = part_lse;
   const int64_t grid = (int64_t)a.n_qtiles * C * B * H;
@@ -398,6 +410,7 @@ attn_status_t attn_splitkv_fwd(const void* q, const void* k, const void* v, cons
   a.chunk = chunk;
   a.C = C;
   a.n_qtiles = (Tq + kBM - 1) / kBM;
+  a.order_b = (B > 1 && B <= kMaxOrderedBatch) ? 1 : 0;
   a.part_out = part_out;
   a.part_lse = part_lse;
   a.counters = counters;
@@ -413,13 +426,13 @@ attn_status_t attn_lse_combine(const float* part_out, const float* part_lse, int
   if (B < 0 || H < 0 || C < 0 || Tq < 0 || D < 0) return ATTN_ERR_SHAPE;
   if (D != 64 && D != 128 && D != 256) return ATTN_ERR_UNSUPPORTED;
   if (B == 0 || H == 0 || Tq == 0) return ATTN_OK;
-  if (!out || (C > 0 && (!part_out || !part_lse))) return ATTN_ERR_NULLPTR;
-  if (!aligned16(out) || (lse && !aligned4(lse))) return ATTN_ERR_ALIGN;
-  if (C > 0 && (!aligned16(part_out) || !aligned4(part_lse))) return ATTN_ERR_ALIGN;
   const int64_t rows = (int64_t)B * H * Tq;
   const int rows_per_wg = 1024 / D;
   const int64_t grid = (rows + rows_per_wg - 1) / rows_per_wg;
-  if (grid > kMaxI32) return ATTN_ERR_SHAPE;
+  if (!grid_fits(grid, 256)) return ATTN_ERR_SHAPE;  // sizes before pointers
+  if (!out || (C > 0 && (!part_out || !part_lse))) return ATTN_ERR_NULLPTR;
+  if (!aligned16(out) || (lse && !aligned4(lse))) return ATTN_ERR_ALIGN;
+  if (C > 0 && (!aligned16(part_out) || !aligned4(part_lse))) return ATTN_ERR_ALIGN;
   CombineArgs a{part_out, part_lse, rows, C, Tq, out, lse};
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   if (verbose())

@@ -223,3 +223,58 @@ def test_single_launch_split_argument_errors(L):
     assert call(out=PM) == ALIGN
     assert call(lse=ctypes.c_void_p(4097)) == ALIGN
     assert call(B=0, counters=None, out=None) == OK
+
+
+# A 1-D dispatch counts work-items (workgroups x threads) in 32 bits: 256-thread launches hold
+# at most 2^24 - 1 workgroups, the 512-thread mask launch 2^23 - 1.  Sizes are checked before
+# pointers, so a call just inside the limit with a NULL pointer returns ATTN_ERR_NULLPTR (and
+# launches nothing), the same call one workgroup past it ATTN_ERR_SHAPE.
+MAX_WG = (2**32 - 1) // 256
+
+
+def test_launch_limits_forward_and_split(L):
+    assert MAX_WG == 2**24 - 1
+    # fused forward: B * H * ceil(Tq / 128) workgroups
+    assert fwd(L, q=None, Tq=128 * MAX_WG) == NULLPTR
+    assert fwd(L, q=None, Tq=128 * MAX_WG + 1) == SHAPE
+    assert fwd(L, q=None, B=2**8, H=2**8, Tq=128 * 255) == NULLPTR  # 2^24 - 2^16 workgroups
+    assert fwd(L, q=None, B=2**8, H=2**8, Tq=128 * 256) == SHAPE  # exactly 2^24
+    assert fwd(L, q=None, B=2**8, H=2**8, Tq=128 * 4096) == SHAPE  # between 2^24 and 2^31 workgroups
+    # split partial: B * H * ceil(Tq / 128) * C
+    assert split(L, po=None, B=MAX_WG) == NULLPTR
+    assert split(L, po=None, B=MAX_WG + 1) == SHAPE
+    assert split(L, po=None, B=MAX_WG // 3, S=192) == NULLPTR  # C = 3
+    assert split(L, po=None, B=MAX_WG // 3 + 1, S=192) == SHAPE
+
+
+def test_launch_limits_single_launch_split(L):
+    def call(**kw):
+        a = dict(B=1, H=1, Tq=1, S=64)
+        a.update(kw)
+        return L.attn_splitkv_fwd(P, P, P, P, a["B"], a["H"], a["Tq"], a["S"], 64, 0.125, BF16, 64, P, P,
+                                  None, P, None, None)
+
+    assert call(B=MAX_WG) == NULLPTR  # counters NULL: the size check passed
+    assert call(B=MAX_WG + 1) == SHAPE
+
+
+def test_launch_limits_combine_mask_and_backward(L):
+    # merge: 1024 / D rows per workgroup
+    assert combine(L, out=None, Tq=16 * MAX_WG, D=64) == NULLPTR
+    assert combine(L, out=None, Tq=16 * MAX_WG + 1, D=64) == SHAPE
+    assert combine(L, out=None, Tq=4 * MAX_WG, D=256) == NULLPTR
+    assert combine(L, out=None, Tq=4 * MAX_WG + 1, D=256) == SHAPE
+    # mask detector: one 512-thread workgroup per row
+    mask_max = (2**32 - 1) // 512
+    assert L.attn_prefix_mask_to_kv_len(P, mask_max, 8, 8, None, None) == NULLPTR
+    assert L.attn_prefix_mask_to_kv_len(P, mask_max + 1, 8, 8, None, None) == SHAPE
+
+    def bwd(B=1, H=1, Tq=8, S=8, D=256, kv=None):
+        return L.attn_prefix_bwd(P, P, P, kv, P, P, P, B, H, Tq, S, D, 0.125, BF16, P, P, P, P, None)
+
+    # delta: 2048 / D rows per workgroup (8 at D = 256)
+    assert bwd(Tq=8 * MAX_WG) == NULLPTR
+    assert bwd(Tq=8 * MAX_WG + 1) == SHAPE
+    # dk/dv: B * H * ceil(S / 128) workgroups
+    assert bwd(B=MAX_WG, Tq=0, S=128, D=64) == NULLPTR
+    assert bwd(B=MAX_WG + 1, Tq=0, S=128, D=64) == SHAPE
