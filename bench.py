@@ -63,6 +63,48 @@ def traffic_from_profile(name: str, src_hash: str):
     return float(m_bytes.group(1))
 
 
+def blas_vendor() -> str:
+    """BLAS library numpy calls (the oracle's matrix products run there)."""
+    try:
+        from threadpoolctl import threadpool_info
+
+        libs = [f"{p.get('internal_api')} {p.get('version')} ({p.get('num_threads')} threads)"
+                for p in threadpool_info() if p.get("user_api") == "blas"]
+        if libs:
+            return "; ".join(libs)
+    except Exception:  # pragma: no cover
+        pass
+    try:
+        import numpy as np
+
+        cfg = np.show_config(mode="dicts")
+        blas = cfg.get("Build Dependencies", {}).get("blas", {})
+        return f"{blas.get('name')} {blas.get('version')}"
+    except Exception:  # pragma: no cover
+        return "unknown"
+
+
+BF16_TOL = {"out_max_abs": 2e-2, "out_rel_l2": 5e-3, "lse_max_abs": 1e-3}
+
+
+def parity_stats(np, got_out, got_lse, ref_out, ref_lse) -> dict:
+    d = got_out - ref_out
+    fin = np.isfinite(ref_lse)
+    return {
+        "out_max_abs": float(np.abs(d).max()),
+        "out_rel_l2": float(np.linalg.norm(d) / np.linalg.norm(ref_out)),
+        "lse_max_abs": float(np.abs(got_lse[fin] - ref_lse[fin]).max()) if fin.any() else 0.0,
+        "finite": bool(np.isfinite(got_out).all() and np.array_equal(np.isneginf(got_lse), np.isneginf(ref_lse))),
+    }
+
+
+def parity_failures(p: dict) -> list:
+    bad = [f"{k} {p[k]:.3e} > {t:.0e}" for k, t in BF16_TOL.items() if not p[k] <= t]
+    if not p["finite"]:
+        bad.append("non-finite output or -inf pattern differs")
+    return bad
+
+
 def time_launches(fn, steps: int, torch):
     """Run fn() `steps` times with HIP events around each call on the current stream."""
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
@@ -106,7 +148,7 @@ def main() -> int:
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--no-splitkv", action="store_true", help="skip the split-KV workload")
-    ap.add_argument("--no-backward", action="store_true", help="skip the backward workload")
+    ap.add_argument("--no-backward", action="store_true", help="skip the backward workloads")
     ap.add_argument("--no-icl16k", action="store_true", help="skip the warm / MALL-scrubbed 16k ICL leg")
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle timing and parity sample")
     ap.add_argument("--cpu-rows", type=int, default=4096, help="oracle query rows per head for the CPU baseline")
@@ -183,6 +225,8 @@ def main() -> int:
         "kernel_source_sha256_16": src_hash,
     }
 
+    invalid = []  # parity failures of timed outputs: the line then carries no value
+
     # -------------------------------------------------- CPU baseline + parity
     if not args.no_cpu_baseline:
         from oracle import ref_prefix_fwd  # test infrastructure: used only for this leg
@@ -209,18 +253,19 @@ def main() -> int:
             "kind": "oracle",
             "sample": f"fp64 numpy oracle on {rows.shape[1]} seeded query rows per head x {w.B * w.H} heads "
                       f"against all {int(lens.max())} valid keys ({sample_flops:.3e} FLOP in {t_cpu:.2f} s)",
+            "blas": blas_vendor(),
+            "host_cores": cores,
+            "full_config_s_extrapolated": round(t_cpu * flops / sample_flops, 1),
+            "extrapolation": "extrapolated, not measured: the sample's time scaled by the full launch's FLOP "
+                             f"({flops:.4e} / {sample_flops:.4e})",
         }
         go = torch.gather(out, 2, idx[..., None].expand(-1, -1, -1, w.D)).double().cpu().numpy()
         gl = torch.gather(lse, 2, idx).double().cpu().numpy()
-        d = go - ro
-        result["parity"] = {
-            "rows_checked": int(rows.size),
-            "out_max_abs": float(np.abs(d).max()),
-            "out_rel_l2": float(np.linalg.norm(d) / np.linalg.norm(ro)),
-            "lse_max_abs": float(np.abs(gl - rl).max()),
-            "tolerance": "max_abs <= 2e-2 and rel_l2 <= 5e-3 (bf16), lse <= 1e-3",
-        }
+        par = parity_stats(np, go, gl, ro, rl)
+        result["parity"] = dict(rows_checked=int(rows.size), **par,
+                                tolerance="max_abs <= 2e-2 and rel_l2 <= 5e-3 (bf16), lse <= 1e-3")
         log(f"parity: {result['parity']}")
+        invalid += [f"{w.name}: {m}" for m in parity_failures(par)]
         del k_h, v_h
 
     del q, k, v, out, lse
@@ -283,6 +328,37 @@ def main() -> int:
                 "bytes_counted": "Q + valid K/V + fp32 partial write",
             },
         }
+        if not args.no_cpu_baseline:
+            # the oracle on whole sequences of the timed output (the first and a seeded one):
+            # parity of the split-KV leg, and its CPU baseline in the same unit
+            from oracle import ref_lse_combine, ref_splitkv_partial
+
+            seqs = sorted({0, int(np.random.default_rng(ws.seed + 11).integers(1, ws.B))})
+            t_cpu, pars = 0.0, []
+            for b in seqs:
+                n = int(slens[b])
+                qb = q[b:b + 1].float().cpu().numpy().astype(np.float64)
+                kb = k[b:b + 1].float().cpu().numpy().astype(np.float64)
+                vb = v[b:b + 1].float().cpu().numpy().astype(np.float64)
+                t0 = time.perf_counter()
+                rpo, rpl = ref_splitkv_partial(qb, kb, vb, [n], ws.scale, ws.chunk)
+                ro, rl = ref_lse_combine(rpo, rpl, axis=2)
+                t_cpu += time.perf_counter() - t0
+                pars.append(parity_stats(np, out[b:b + 1].double().cpu().numpy(), lse[b:b + 1].double().cpu().numpy(),
+                                         ro, rl))
+            seq_bytes = alg_bytes / ws.B * len(seqs)
+            par = {kk: max(p[kk] for p in pars) for kk in BF16_TOL}
+            par["finite"] = all(p["finite"] for p in pars)
+            result["splitkv"]["parity"] = dict(sequences_checked=seqs, heads_rows="all 4 heads x 128 rows", **par)
+            result["splitkv"]["cpu_baseline"] = {
+                "value": round(seq_bytes / t_cpu / 1e9, 4), "unit": "GB/s (algorithmic)", "cores": int(len(os.sched_getaffinity(0))),
+                "kind": "oracle",
+                "sample": f"fp64 numpy oracle (chunk partials + LSE merge) on sequences {seqs}, all heads and rows "
+                          f"({t_cpu:.2f} s)",
+                "full_config_s_extrapolated": round(t_cpu * ws.B / len(seqs), 1),
+            }
+            log(f"split-KV parity: {result['splitkv']['parity']}")
+            invalid += [f"{ws.name}: {m}" for m in parity_failures(par)]
         del q, k, v, po, pl, out, lse
         torch.cuda.empty_cache()
 
@@ -383,6 +459,40 @@ def main() -> int:
         del q, k, v, out, lse, dout, dq, dk, dv, delta
         torch.cuda.empty_cache()
 
+        # the ICL head size, D = 256, at the 16k block
+        wi = WORKLOADS["icl_16k"]
+        log(f"generating {wi.name} backward: B={wi.B} H={wi.H} D={wi.D} Tq={wi.Tq} S={wi.S}")
+        q, k, v, kv = make_workload(wi, device="cuda")
+        ilens = wi.lens()
+        ipairs = float(wi.H) * wi.Tq * float(ilens.sum())
+        out = torch.empty_like(q)
+        lse = torch.empty((wi.B, wi.H, wi.Tq), dtype=torch.float32, device="cuda")
+        g = torch.Generator(device="cpu").manual_seed(wi.seed + 77)
+        dout = torch.randn(q.shape, generator=g, dtype=torch.float32).to(torch.bfloat16).to("cuda")
+        dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+        delta = torch.empty_like(lse)
+        _lib.attn_prefix_fwd(q, k, v, kv, wi.scale, out=out, lse=lse)
+
+        def bwd_i():
+            _lib.attn_prefix_bwd(q, k, v, kv, out, dout, lse, wi.scale, dq=dq, dk=dk, dv=dv, delta=delta)
+
+        for _ in range(args.warmup):
+            bwd_i()
+        torch.cuda.synchronize()
+        _, ms_i = time_launches(bwd_i, steps, torch)
+        t_i = sum(ms_i) / len(ms_i)
+        alg_i = 10.0 * wi.D * ipairs
+        log(f"backward {wi.name}: {t_i:.3f} ms, {alg_i / (t_i * 1e-3) / 1e12:.1f} TFLOP/s")
+        result["backward_d256"] = {
+            "workload": wi.name, "B": wi.B, "H": wi.H, "head_dim": wi.D, "T_q": wi.Tq, "S": wi.S,
+            "backward_ms": round(t_i, 4), "value": round(alg_i / (t_i * 1e-3) / 1e12, 2),
+            "unit": "TFLOP/s (algorithmic: 10 D per (query, valid key) pair and head)",
+            "pct_mfma_peak": round(100 * alg_i / (t_i * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 2),
+            "kernels": "bwd_delta_kernel, bwd_dq_slot_kernel (S, dP, dQ), bwd_dkdv_slot_kernel (S, dP, dV, dK)",
+        }
+        del q, k, v, out, lse, dout, dq, dk, dv, delta
+        torch.cuda.empty_cache()
+
     if args.copy_calibration:
         src = torch.empty(1 << 28, dtype=torch.float32, device="cuda").fill_(1.0)
         dst = torch.empty_like(src)
@@ -390,8 +500,13 @@ def main() -> int:
         torch.cuda.synchronize()
         log("copy calibration: 1 GiB read + 1 GiB written")
 
+    if invalid:
+        # a timed output that misses the oracle's tolerance voids the measurement
+        result["value"] = None
+        result["invalid"] = invalid
+        log(f"PARITY FAILED: {invalid}")
     print(json.dumps(result), flush=True)
-    return 0
+    return 1 if invalid else 0
 
 
 if __name__ == "__main__":

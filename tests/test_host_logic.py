@@ -79,3 +79,20 @@ def test_bench_refuses_more_than_one_gpu():
                          text=True, timeout=120)
     assert res.returncode == 2
     assert "one GPU" in res.stderr
+
+
+def test_bench_parity_gate():
+    """A timed output outside the bf16 tolerance voids the bench line (value null, exit 1)."""
+    sys.path.insert(0, ROOT)
+    import bench
+
+    ref = np.ones((2, 3))
+    lse = np.array([1.0, -np.inf])
+    good = bench.parity_stats(np, ref + 1e-3, lse, ref, lse)
+    assert bench.parity_failures(good) == []
+    assert len(bench.parity_failures(bench.parity_stats(np, ref + 3e-2, lse, ref, lse))) == 2  # max-abs and rel-L2
+    assert len(bench.parity_failures(bench.parity_stats(np, ref, lse + np.array([2e-3, 0.0]), ref, lse))) == 1
+    nan_out = ref.copy()
+    nan_out[0, 0] = np.nan
+    assert bench.parity_failures(bench.parity_stats(np, nan_out, lse, ref, lse))  # NaN never passes
+    assert bench.parity_failures(bench.parity_stats(np, ref, np.array([1.0, 0.0]), ref, lse))  # -inf pattern
