@@ -191,6 +191,22 @@ attn_status_t attn_prefix_bwd(const void* q, const void* k, const void* v, const
                               const void* dout, const float* lse, int B, int H, int Tq, int S, int D, float scale,
                               attn_dtype_t dtype, float* delta, void* dq, void* dk, void* dv, void* stream);
 
+/* attn_prefix_bwd without the `delta` workspace, for callers that cannot allocate
+ * device memory: code under HIP graph capture, tight training loops, harnesses that
+ * forbid hipMalloc.  The same computation, arguments and results as attn_prefix_bwd;
+ * delta lives instead in a device array of the library, 16 MiB per GPU, which every
+ * GPU the library runs on holds from the library's load to the end of the process.
+ * The call allocates nothing and sets no memory (delta is written in full before it
+ * is read).  Limit: B * H * Tq <= 4,194,304 rows, else ATTN_ERR_SHAPE before any HIP
+ * call.  Every call on one GPU uses that GPU's one array: calls that overlap in time
+ * on one GPU (on different streams, or from different host threads without ordering)
+ * race on it and must be serialized by the caller.  The first call on a device looks
+ * up the array's device address (ATTN_ERR_HIP if that fails). */
+attn_status_t attn_prefix_bwd_noalloc(const void* q, const void* k, const void* v, const int32_t* kv_len,
+                                      const void* out, const void* dout, const float* lse, int B, int H, int Tq,
+                                      int S, int D, float scale, attn_dtype_t dtype, void* dq, void* dk, void* dv,
+                                      void* stream);
+
 /* Host helper: number of chunks ceil(S / chunk); -1 if chunk <= 0 or S < 0. */
 int attn_splitkv_num_chunks(int S, int chunk);
 

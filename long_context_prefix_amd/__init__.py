@@ -13,7 +13,9 @@ The public calls mirror the C ABI of ``libattnprefix.so``:
   a [B, 1, 1, S] boolean prefix mask turned into lengths on the device, and an
   SDPA-style entry that raises on any other mask;
 * ``attn_prefix_bwd(...)`` / ``prefix_attention(q, k, v, kv_len)`` -- the
-  gradients, and a differentiable wrapper for training on ragged batches.
+  gradients, and a differentiable wrapper for training on ragged batches;
+  ``attn_prefix_bwd_noalloc(...)`` computes them with no workspace argument and
+  no allocation, for callers that cannot allocate.
 
 The library is loaded on first use; a missing build raises instead of falling
 back to anything else.
@@ -23,6 +25,7 @@ from ._lib import (  # noqa: F401
     AttnError,
     attn_lse_combine,
     attn_prefix_bwd,
+    attn_prefix_bwd_noalloc,
     attn_prefix_fwd,
     attn_prefix_mask_to_kv_len,
     attn_splitkv_fwd,

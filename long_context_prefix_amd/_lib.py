@@ -24,7 +24,8 @@ STATUS_NAMES = {
 }
 ATTN_BF16, ATTN_F32 = 0, 1
 EXPORTED = ("attn_version", "attn_prefix_fwd", "attn_splitkv_partial", "attn_lse_combine", "attn_splitkv_fwd",
-            "attn_prefix_mask_to_kv_len", "attn_prefix_bwd", "attn_splitkv_num_chunks", "attn_status_string")
+            "attn_prefix_mask_to_kv_len", "attn_prefix_bwd", "attn_prefix_bwd_noalloc", "attn_splitkv_num_chunks",
+            "attn_status_string")
 
 _lib = None
 
@@ -59,6 +60,8 @@ def load() -> ctypes.CDLL:
     L.attn_splitkv_fwd.argtypes = [vp, vp, vp, vp, i32, i32, i32, i32, i32, f32, i32, i32, vp, vp, vp, vp, vp, vp]
     L.attn_prefix_bwd.restype = i32
     L.attn_prefix_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, f32, i32, vp, vp, vp, vp, vp]
+    L.attn_prefix_bwd_noalloc.restype = i32
+    L.attn_prefix_bwd_noalloc.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, f32, i32, vp, vp, vp, vp]
     L.attn_splitkv_num_chunks.restype = i32
     L.attn_splitkv_num_chunks.argtypes = [i32, i32]
     L.attn_status_string.restype = ctypes.c_char_p
@@ -279,6 +282,27 @@ def attn_prefix_bwd(q, k, v, kv_len, out, dout, lse, scale: Optional[float] = No
                                   B, H, Tq, S, D, scale, _dtype_code(q), _ptr(delta), _ptr(dq), _ptr(dk), _ptr(dv),
                                   _stream(dev))
     _check("attn_prefix_bwd", code)
+    return dq, dk, dv
+
+
+def attn_prefix_bwd_noalloc(q, k, v, kv_len, out, dout, lse, dq, dk, dv, scale: Optional[float] = None):
+    """attn_prefix_bwd into caller-provided dq, dk, dv, with no workspace argument: the
+    library keeps delta in a device array of its own (at most 4,194,304 rows of
+    B * H * Tq), so the call allocates nothing.  Calls that overlap in time on one GPU race
+    on that array."""
+    B, H, Tq, S, D, dev = _fwd_shapes(q, k, v, kv_len)
+    scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
+    for t, ref, name in ((out, q, "out"), (dout, q, "dout"), (dq, q, "dq"), (dk, k, "dk"), (dv, v, "dv")):
+        _require(t, name, dev)
+        if t.shape != ref.shape or t.dtype != ref.dtype:
+            raise ValueError(f"{name} has the wrong shape or dtype")
+    _require(lse, "lse", dev)
+    if lse.shape != (B, H, Tq) or lse.dtype != torch.float32:
+        raise ValueError("lse must be fp32 [B, H, Tq]")
+    code = load().attn_prefix_bwd_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(kv_len), _ptr(out), _ptr(dout), _ptr(lse),
+                                          B, H, Tq, S, D, scale, _dtype_code(q), _ptr(dq), _ptr(dk), _ptr(dv),
+                                          _stream(dev))
+    _check("attn_prefix_bwd_noalloc", code)
     return dq, dk, dv
 
 

@@ -8,6 +8,7 @@
 #include <string.h>
 
 #include <atomic>
+#include <mutex>
 
 #include "attn_bwd_kernels.hpp"
 #include "attn_kernels.hpp"
@@ -231,27 +232,42 @@ attn_status_t launch_bwd(const BwdArgs& base, int64_t rows, int64_t grid_dq, int
 
 }  // namespace
 
-extern "C" {
+// Scratch of the allocation-free backward (attn_prefix_bwd_noalloc): its delta rows,
+// rowsum(dout * out) in fp32, at most kNoAllocMaxRows of them.  A device array of the
+// library's code object: every GPU the library runs on holds its own copy from the load
+// of the library to the end of the process.  In host code `scratch` only names the
+// symbol; its device address comes from hipGetSymbolAddress, per device.
+constexpr int64_t kNoAllocMaxRows = int64_t(1) << 22;  // 16 MiB of fp32 per GPU
+static __device__ __align__(256) float scratch[kNoAllocMaxRows];
 
-int attn_version(void) { return (0 << 16) | (2 << 8) | 0; }
+namespace {
 
-attn_status_t attn_prefix_mask_to_kv_len(const uint8_t* mask, int B, int S, int64_t row_stride, int32_t* kv_len,
-                                         void* stream) {
-  if (B < 0 || S < 0 || row_stride < 0) return ATTN_ERR_SHAPE;
-  if (B == 0) return ATTN_OK;
-  if (!grid_fits(B, kMaskThreads)) return ATTN_ERR_SHAPE;
-  if (!kv_len || (S > 0 && !mask)) return ATTN_ERR_NULLPTR;
-  if (!aligned4(kv_len)) return ATTN_ERR_ALIGN;
-  if (verbose()) fprintf(stderr, "[attn_prefix] prefix_mask_to_kv_len B=%d S=%d\n", B, S);
-  (void)hipGetLastError();
-  hipLaunchKernelGGL(prefix_mask_kernel, dim3((unsigned)B), dim3(kMaskThreads), 0,
-                     reinterpret_cast<hipStream_t>(stream), mask, S, row_stride, kv_len);
-  return hipGetLastError() == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
+constexpr int kMaxDevices = 64;
+
+// The device address of `scratch` on the current device, looked up once per device (with
+// that device current) and kept; NULL when the lookup fails.
+float* noalloc_scratch() {
+  static std::atomic<float*> cached[kMaxDevices];  // zero-initialized: not yet looked up
+  static std::mutex mu;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  float* p = cached[dev].load(std::memory_order_acquire);
+  if (p) return p;
+  std::lock_guard<std::mutex> lock(mu);
+  p = cached[dev].load(std::memory_order_relaxed);
+  if (!p) {
+    void* addr = nullptr;
+    if (hipGetSymbolAddress(&addr, HIP_SYMBOL(scratch)) != hipSuccess || addr == nullptr) return nullptr;
+    p = static_cast<float*>(addr);
+    cached[dev].store(p, std::memory_order_release);
+  }
+  return p;
 }
 
-attn_status_t attn_prefix_bwd(const void* q, const void* k, const void* v, const int32_t* kv_len, const void* out,
-                              const void* dout, const float* lse, int B, int H, int Tq, int S, int D, float scale,
-                              attn_dtype_t dtype, float* delta, void* dq, void* dk, void* dv, void* stream) {
+// The backward, with `delta` from the caller or (noalloc) in the library's scratch array.
+attn_status_t prefix_bwd(const void* q, const void* k, const void* v, const int32_t* kv_len, const void* out,
+                         const void* dout, const float* lse, int B, int H, int Tq, int S, int D, float scale,
+                         attn_dtype_t dtype, float* delta, void* dq, void* dk, void* dv, void* stream, bool noalloc) {
   if (dtype != ATTN_BF16 && dtype != ATTN_F32) return ATTN_ERR_DTYPE;
   if (B < 0 || H < 0 || Tq < 0 || S < 0 || D < 0) return ATTN_ERR_SHAPE;
   if (dtype != ATTN_BF16 || (D != 64 && D != 128 && D != 256)) return ATTN_ERR_UNSUPPORTED;
@@ -265,16 +281,21 @@ attn_status_t attn_prefix_bwd(const void* q, const void* k, const void* v, const
   const int64_t grid_delta = (rows + 256 / (D / 8) - 1) / (256 / (D / 8));
   if (!grid_fits(grid_dq, kThreads) || !grid_fits(grid_dkdv, kThreads) || !grid_fits(grid_delta, 256))
     return ATTN_ERR_SHAPE;
+  if (noalloc && rows > kNoAllocMaxRows) return ATTN_ERR_SHAPE;
   if (!kv_len) return ATTN_ERR_NULLPTR;
-  if (Tq > 0 && (!q || !out || !dout || !lse || !delta || !dq)) return ATTN_ERR_NULLPTR;
+  if (Tq > 0 && (!q || !out || !dout || !lse || (!noalloc && !delta) || !dq)) return ATTN_ERR_NULLPTR;
   if (S > 0 && (!dk || !dv)) return ATTN_ERR_NULLPTR;
   if (S > 0 && Tq > 0 && (!k || !v)) return ATTN_ERR_NULLPTR;
   if (!aligned4(kv_len)) return ATTN_ERR_ALIGN;
   if (Tq > 0 && (!aligned16(q) || !aligned16(out) || !aligned16(dout) || !aligned16(dq) || !aligned4(lse) ||
-                 !aligned4(delta)))
+                 (!noalloc && !aligned4(delta))))
     return ATTN_ERR_ALIGN;
   if (S > 0 && (!aligned16(dk) || !aligned16(dv) || (Tq > 0 && (!aligned16(k) || !aligned16(v)))))
     return ATTN_ERR_ALIGN;
+  if (noalloc) {
+    delta = noalloc_scratch();  // the first call on a device looks the address up
+    if (!delta) return ATTN_ERR_HIP;
+  }
   BwdArgs a{};
   a.q = q;
   a.k = k;
@@ -296,11 +317,44 @@ attn_status_t attn_prefix_bwd(const void* q, const void* k, const void* v, const
   a.dv = dv;
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   if (verbose())
-    fprintf(stderr, "[attn_prefix] prefix_bwd D=%d B=%d H=%d Tq=%d S=%d grid dq=%lld dkdv=%lld\n", D, B, H, Tq, S,
-            (long long)grid_dq, (long long)grid_dkdv);
+    fprintf(stderr, "[attn_prefix] prefix_bwd%s D=%d B=%d H=%d Tq=%d S=%d grid dq=%lld dkdv=%lld\n",
+            noalloc ? "_noalloc" : "", D, B, H, Tq, S, (long long)grid_dq, (long long)grid_dkdv);
   if (D == 64) return launch_bwd<64, 2, 2>(a, rows, grid_dq, grid_dkdv, st);
   if (D == 128) return launch_bwd<128, 2, 0>(a, rows, grid_dq, grid_dkdv, st);
   return launch_bwd<256, 1, 1>(a, rows, grid_dq, grid_dkdv, st);
+}
+
+}  // namespace
+
+extern "C" {
+
+int attn_version(void) { return (0 << 16) | (2 << 8) | 0; }
+
+attn_status_t attn_prefix_mask_to_kv_len(const uint8_t* mask, int B, int S, int64_t row_stride, int32_t* kv_len,
+                                         void* stream) {
+  if (B < 0 || S < 0 || row_stride < 0) return ATTN_ERR_SHAPE;
+  if (B == 0) return ATTN_OK;
+  if (!grid_fits(B, kMaskThreads)) return ATTN_ERR_SHAPE;
+  if (!kv_len || (S > 0 && !mask)) return ATTN_ERR_NULLPTR;
+  if (!aligned4(kv_len)) return ATTN_ERR_ALIGN;
+  if (verbose()) fprintf(stderr, "[attn_prefix] prefix_mask_to_kv_len B=%d S=%d\n", B, S);
+  (void)hipGetLastError();
+  hipLaunchKernelGGL(prefix_mask_kernel, dim3((unsigned)B), dim3(kMaskThreads), 0,
+                     reinterpret_cast<hipStream_t>(stream), mask, S, row_stride, kv_len);
+  return hipGetLastError() == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
+}
+
+attn_status_t attn_prefix_bwd(const void* q, const void* k, const void* v, const int32_t* kv_len, const void* out,
+                              const void* dout, const float* lse, int B, int H, int Tq, int S, int D, float scale,
+                              attn_dtype_t dtype, float* delta, void* dq, void* dk, void* dv, void* stream) {
+  return prefix_bwd(q, k, v, kv_len, out, dout, lse, B, H, Tq, S, D, scale, dtype, delta, dq, dk, dv, stream, false);
+}
+
+attn_status_t attn_prefix_bwd_noalloc(const void* q, const void* k, const void* v, const int32_t* kv_len,
+                                      const void* out, const void* dout, const float* lse, int B, int H, int Tq,
+                                      int S, int D, float scale, attn_dtype_t dtype, void* dq, void* dk, void* dv,
+                                      void* stream) {
+  return prefix_bwd(q, k, v, kv_len, out, dout, lse, B, H, Tq, S, D, scale, dtype, nullptr, dq, dk, dv, stream, true);
 }
 
 int attn_splitkv_num_chunks(int S, int chunk) {
