@@ -315,11 +315,20 @@ void bwd_dkdv_slot_kernel(BwdArgs a) {
   auto g_tile = [&](int t) { return make_rsrc(gg + (int64_t)t * kBN * D, (uint32_t)nq_of(t) * (D * 2)); };
   const float* lse_bh = a.lse + bh * a.Tq;
   const float* del_bh = a.delta + bh * a.Tq;
-  auto stat_load = [&](int t) -> float {
-    const int qi = t * kBN + (tid & 63);
-    if (tid < 64) return qi < a.Tq ? lse_bh[qi] * kLog2e : __builtin_inff();
-    if (tid < 128) return qi < a.Tq ? del_bh[qi] : 0.0f;
-    return 0.0f;
+  // Per-query statistics of query tile t: wave 0 fetches lse, wave 1 delta, one query per
+  // lane.  stat_fetch only issues the load (a buffer load over the tile's valid queries, so
+  // lanes past Tq read 0 without a branch); stat_value forms the value when it is written to
+  // LDS at the end of the iteration, so the load's latency hides behind the whole tile
+  // instead of stalling its first slots.
+  auto stat_fetch = [&](int t) -> float {
+    if (wave_u >= 2) return 0.0f;
+    const int valid = min(max(a.Tq - t * kBN, 0), kBN);
+    const __amdgpu_buffer_rsrc_t rs = make_rsrc((wave_u == 0 ? lse_bh : del_bh) + (int64_t)t * kBN, (uint32_t)valid * 4);
+    return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rs, (uint32_t)lane * 4, 0, 0));
+  };
+  auto stat_value = [&](int t, float raw) -> float {
+    if (wave_u != 0) return raw;
+    return t * kBN + lane < a.Tq ? raw * kLog2e : __builtin_inff();
   };
 
   typename P::QFrag kf, vf;
@@ -340,7 +349,7 @@ void bwd_dkdv_slot_kernel(BwdArgs a) {
   P::dma_tile(q_tile(0), qb_(0), wave_u, lane);
   P::dma_tile(g_tile(0), gb_(0), wave_u, lane);
   {
-    const float x = stat_load(0);
+    const float x = stat_value(0, stat_fetch(0));
     if (tid < 128) stat[0][tid >> 6][tid & 63] = x;
   }
   __builtin_amdgcn_s_waitcnt(0x0F70);
@@ -351,7 +360,7 @@ void bwd_dkdv_slot_kernel(BwdArgs a) {
     const lds_char* gt_ = gb_(cur);
     // past the last tile the resources are empty: the loads zero-fill a buffer never read
     const __amdgpu_buffer_rsrc_t q_rs = q_tile(t + 1), g_rs = g_tile(t + 1);
-    const float next_stat = stat_load(t + 1);
+    const float next_raw = stat_fetch(t + 1);
     f32x16 s[2], dp[2];
     u32x4 ppk[4], dpk[4];
     float p8[8], d8[8];
@@ -450,7 +459,7 @@ void bwd_dkdv_slot_kernel(BwdArgs a) {
       if (j + R < NC) fr[j % R] = frag_cd(1, j + R);
       __builtin_amdgcn_sched_barrier(0);
     }
-    if (tid < 128) stat[cur ^ 1][tid >> 6][tid & 63] = next_stat;
+    if (tid < 128) stat[cur ^ 1][tid >> 6][tid & 63] = stat_value(t + 1, next_raw);
     __builtin_amdgcn_s_waitcnt(0x0F70);
     lds_barrier();
   }
@@ -531,11 +540,20 @@ void bwd_dkdv_pipe_kernel(BwdArgs a) {
   auto g_tile = [&](int t) { return make_rsrc(gg + (int64_t)t * kBN * D, (uint32_t)nq_of(t) * (D * 2)); };
   const float* lse_bh = a.lse + bh * a.Tq;
   const float* del_bh = a.delta + bh * a.Tq;
-  auto stat_load = [&](int t) -> float {
-    const int qi = t * kBN + (tid & 63);
-    if (tid < 64) return qi < a.Tq ? lse_bh[qi] * kLog2e : __builtin_inff();
-    if (tid < 128) return qi < a.Tq ? del_bh[qi] : 0.0f;
-    return 0.0f;
+  // Per-query statistics of query tile t: wave 0 fetches lse, wave 1 delta, one query per
+  // lane.  stat_fetch only issues the load (a buffer load over the tile's valid queries, so
+  // lanes past Tq read 0 without a branch); stat_value forms the value when it is written to
+  // LDS at the end of the iteration, so the load's latency hides behind the whole tile
+  // instead of stalling its first slots.
+  auto stat_fetch = [&](int t) -> float {
+    if (wave_u >= 2) return 0.0f;
+    const int valid = min(max(a.Tq - t * kBN, 0), kBN);
+    const __amdgpu_buffer_rsrc_t rs = make_rsrc((wave_u == 0 ? lse_bh : del_bh) + (int64_t)t * kBN, (uint32_t)valid * 4);
+    return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rs, (uint32_t)lane * 4, 0, 0));
+  };
+  auto stat_value = [&](int t, float raw) -> float {
+    if (wave_u != 0) return raw;
+    return t * kBN + lane < a.Tq ? raw * kLog2e : __builtin_inff();
   };
 
   typename P::QFrag kf, vf;
@@ -559,8 +577,8 @@ void bwd_dkdv_pipe_kernel(BwdArgs a) {
   P::dma_tile(q_tile(1), qb_(1), wave_u, lane);  // empty past Tq: zero fill
   P::dma_tile(g_tile(1), gb_(1), wave_u, lane);
   {
-    const float x0 = stat_load(0);
-    const float x1 = stat_load(1);
+    const float x0 = stat_value(0, stat_fetch(0));
+    const float x1 = stat_value(1, stat_fetch(1));
     if (tid < 128) {
       stat[0][tid >> 6][tid & 63] = x0;
       stat[1][tid >> 6][tid & 63] = x1;
@@ -577,7 +595,7 @@ void bwd_dkdv_pipe_kernel(BwdArgs a) {
                        f32x16 (&dn)[kBN / 32]) {
     const int bc = t % 3, bn = (t + 1) % 3, bf = (t + 2) % 3;
     const __amdgpu_buffer_rsrc_t q_rs = q_tile(t + 2), g_rs = g_tile(t + 2);
-    const float next_stat = stat_load(t + 2);
+    const float next_raw = stat_fetch(t + 2);
     // this tile's per-query statistics, four queries at a time: softmax element e is register
     // e % 16 of block e / 16, query 32 (e / 16) + 8 ((e % 16) / 4) + 4 h + e % 4
     auto stat4 = [&](int g, int which) {
@@ -645,7 +663,7 @@ void bwd_dkdv_pipe_kernel(BwdArgs a) {
       }
       __builtin_amdgcn_sched_barrier(0);
     }
-    if (tid < 128) stat[bf][tid >> 6][tid & 63] = next_stat;
+    if (tid < 128) stat[bf][tid >> 6][tid & 63] = stat_value(t + 2, next_raw);
     __builtin_amdgcn_s_waitcnt(0x0F70);  // this wave's tile loads have landed
     lds_barrier();
   };
