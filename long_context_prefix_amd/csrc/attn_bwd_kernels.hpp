@@ -152,9 +152,28 @@ void bwd_dq_slot_kernel(BwdArgs a) {
   P::load_q(gf, reinterpret_cast<const uint16_t*>(a.dout) + src_row * D, row_ok, h_half);
   const float L = row_ok ? a.lse[grow] * kLog2e : 0.0f;
   const float dl = row_ok ? a.delta[grow] : 0.0f;
-  const float c = a.scale_log2;
+  float c = a.scale_log2;
+  if (c < 0.0f) {  // c * (q.k) == |c| * ((-q).k): keep c > 0 so that a -inf score gives p = 0
+    c = -c;
+#pragma unroll
+    for (int kk = 0; kk < P::NQ; ++kk) {
+      u32x4 x = __builtin_bit_cast(u32x4, qf.v[kk]) ^ 0x80008000u;
+      qf.v[kk] = __builtin_bit_cast(bf16x8, x);
+    }
+  }
+  c = fmaxf(c, 1.17549435e-38f);  // a zero scale as the smallest normal float (p = 2^-L as for scale 0)
   const int kbase = P::k_base(lane);
   const int vbase = P::v_base(lane);
+  // keys at or past nv of the last tile get s = -inf, so p = 0 and dS = 0 (rare: the key
+  // indices come from an opaque copy of the lane's half, so that they are computed here
+  // instead of being hoisted out of the tile loop into live registers)
+  auto mask_half = [&](f32x16& sh, int hf, int nv) {
+    int hh = h_half;
+    asm volatile("" : "+v"(hh));
+#pragma unroll
+    for (int e = 0; e < 16; ++e)
+      if (st_key(hf, e, hh) >= nv) sh[e] = -__builtin_inff();
+  };
 
   f32x16 acc[D / 32];
 #pragma unroll
@@ -187,8 +206,7 @@ void bwd_dq_slot_kernel(BwdArgs a) {
     };
     // softmax element e (0..15) of half hf: register e of S^T block hf
     auto elem = [&](int hf, int e) {
-      float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[hf][e], c, -L));
-      if (st_key(hf, e, h_half) >= nv) p = 0.0f;
+      const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[hf][e], c, -L));
       d8[e & 7] = p * (dp[hf][e] - dl);
       if ((e & 7) == 7)
         pk[2 * hf + (e >> 3)] = u32x4{pack_bf16x2(d8[0], d8[1]), pack_bf16x2(d8[2], d8[3]),
@@ -218,6 +236,11 @@ void bwd_dq_slot_kernel(BwdArgs a) {
       __builtin_amdgcn_sched_barrier(0);
     }
     xdl_result_guard();  // the softmax below reads the half-0 results
+    if (nv < kBN) {
+      rare_path();
+      mask_half(s[0], 0, nv);
+    }
+    __builtin_amdgcn_sched_barrier(0);
     // phase B: S^T, dP^T of keys 32..63; P and dS of keys 0..31
 #pragma unroll
     for (int j = 0; j < NH; ++j) {
@@ -230,6 +253,11 @@ void bwd_dq_slot_kernel(BwdArgs a) {
       __builtin_amdgcn_sched_barrier(0);
     }
     xdl_result_guard();  // the softmax below reads the half-1 results
+    if (nv < kBN) {
+      rare_path();
+      mask_half(s[1], 1, nv);
+    }
+    __builtin_amdgcn_sched_barrier(0);
     // phase C: dQ^T over keys 0..31; P and dS of keys 32..63
 #pragma unroll
     for (int j = 0; j < NC; ++j) {

@@ -135,3 +135,16 @@ def test_autograd_wrapper_matches_oracle():
     _check("dq", qq.grad, rq, "autograd")
     _check("dk", kk.grad, rk, "autograd")
     _check("dv", vv.grad, rv, "autograd")
+
+
+@pytest.mark.parametrize("scale", [-0.09, 0.0, 0.3])
+@pytest.mark.parametrize("D", [64, 128, 256])
+def test_bwd_scale_sign_and_zero(D, scale):
+    """Negative scales (the dq kernel negates Q internally), scale 0 (uniform weights: every
+    gradient path still runs) and a large scale, on ragged lengths whose last key tiles are
+    partly masked."""
+    B, H, Tq, S = 2, 2, 130, 300
+    lens = [300, 77]
+    log(f"bwd scale={scale} D={D}")
+    q, k, v, kv = make_inputs(B, H, Tq, S, D, lens, "bf16", 1.0, seed=990 + D, device=DEV)
+    _compare(q, k, v, kv, scale, 11, f"bwd scale={scale} D={D}")
