@@ -71,3 +71,51 @@ def test_graph_replays_match_eager():
                                    (kv, out, lse, sout, slse, dq, dk, dv), eager):
             assert torch.equal(got, want), f"replay {rep}: {name} differs from the eager result"
         log(f"graph replay {rep}: identical to eager")
+
+
+def test_graph_with_the_allocation_free_backward():
+    """The allocation-free backward in a captured graph: nothing is allocated at capture or
+    replay (its delta lives in the library's device array), and eager calls of another shape
+    between the replays, which overwrite that array, do not change what a replay computes."""
+    B, H, Tq, S, D = 2, 2, 150, 300, 128
+    lens = [300, 77]
+    q, k, v, kv = make_inputs(B, H, Tq, S, D, lens, "bf16", 1.0, seed=5160, device=DEV)
+    dout = torch.randn(q.shape, generator=torch.Generator().manual_seed(10)).to(torch.bfloat16).to(DEV)
+    scale = 1.0 / math.sqrt(D)
+    out = torch.empty_like(q)
+    lse = torch.empty((B, H, Tq), device=DEV)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    # another shape whose eager calls run between the replays
+    q2, k2, v2, kv2 = make_inputs(3, 1, 400, 200, 64, [200, 5, 150], "bf16", 1.0, seed=5161, device=DEV)
+    out2, lse2 = _lib.attn_prefix_fwd(q2, k2, v2, kv2, 0.125)
+    g2 = tuple(torch.empty_like(t) for t in (q2, k2, v2))
+
+    def step():
+        _lib.attn_prefix_fwd(q, k, v, kv, scale, out=out, lse=lse)
+        _lib.attn_prefix_bwd_noalloc(q, k, v, kv, out, dout, lse, dq, dk, dv, scale)
+
+    step()
+    torch.cuda.synchronize()
+    eager = [t.clone() for t in (out, lse, dq, dk, dv)]
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        step()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    torch.cuda.synchronize()
+    for rep in range(3):
+        _lib.attn_prefix_bwd_noalloc(q2, k2, v2, kv2, out2, out2, lse2, *g2, 0.125)  # overwrites the scratch
+        for t in (out, lse, dq, dk, dv):
+            t.zero_()
+        torch.cuda.synchronize()
+        before = torch.cuda.memory_stats(DEV).get("allocation.all.allocated", 0)
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.cuda.memory_stats(DEV).get("allocation.all.allocated", 0) == before
+        for name, got, want in zip(("out", "lse", "dq", "dk", "dv"), (out, lse, dq, dk, dv), eager):
+            assert torch.equal(got, want), f"replay {rep}: {name} differs from the eager result"
+        log(f"graph replay {rep} with the allocation-free backward: identical to eager")
