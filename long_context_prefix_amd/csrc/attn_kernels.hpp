@@ -157,7 +157,8 @@ struct Bf16Dma {
   static constexpr int NBLK = kBN / RPB;   // blocks per tile (32, 16, 8)
   static constexpr int BLK = 1040;         // padded block stride
   static constexpr int TILE_BYTES = NBLK * BLK;
-  static constexpr int LDS_BYTES = 4 * TILE_BYTES;  // K and V, two buffers each
+  static constexpr int FLAGS = 4 * TILE_BYTES;      // K and V, two buffers each, then
+  static constexpr int LDS_BYTES = FLAGS + 4 * 4;   // one second-pass flag per wave
   static constexpr int NQ = D / 16;
   static constexpr int LPR = ROWB / 16;    // DMA lanes per row
   static constexpr bool kIsF32 = false;
@@ -657,56 +658,82 @@ __device__ __forceinline__ void lds_barrier() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
-// Online-softmax state of one lane (one query row, half of its keys).  The
-// running max m is kept in the scaled log2 domain and is moved only when a
-// tile's max exceeds it by more than kRescaleLog2: probabilities are computed
-// against a possibly stale max, so p <= 2^kRescaleLog2, and the final O / l is
-// unchanged because O and l share that max.  Rescaling O (kept in AGPRs) is
-// therefore rare instead of once per tile.
-constexpr float kRescaleLog2 = 8.0f;
+// Softmax state of one lane of the bf16 kernels, for G query rows (1 in the 32-row kernel,
+// 2 in the 64-row kernel), each with half of its keys in this lane.
+//
+// O is never rescaled inside the tile loop.  All probabilities of a pass are taken
+// against one reference per row: the first tile's (scaled) max.  No per-tile max is
+// taken either: a tile is checked through the sums that the loop forms anyway.  While a
+// lane's sum over a tile stays at or below 2^kSlackLog2, every p of it does too, so the
+// tile's scores are at most the reference + kSlackLog2, and the sums cannot overflow (a
+// row has fewer than 2^22 keys, so this holds for any V below 2^86).  A tile that breaks
+// this marks the pass bad and records its exact max; the workgroup then runs the pass
+// again against max(reference + kSlackLog2, recorded maxima), which every score of the
+// row is at or below.  O / l is the same softmax either way: only the common scale
+// differs.  Natural inputs stay within the slack (a row's scores would have to climb
+// 20 log2 units past its first tile's max), so the second pass is rare; the per-tile max
+// it replaces cost the 32-row kernel 3% of its time.
+constexpr float kSlackLog2 = 20.0f;
 
-template <int D>
-struct Softmax {
-  float m = -__builtin_inff();  // scaled log2-domain max the probabilities are taken against
-  float l = 0.0f;               // this lane's partial row sum (lanes l and l^32 are added at the end)
-
-  // Scaled row max of raw scores s (this lane's keys, then its partner lane's).
-  __device__ __forceinline__ static float row_max(const f32x16 (&s)[kBN / 32], float c) {
-    float mt = fmaxf(s[0][0], s[0][1]);
+template <int G>
+struct PassSoftmax {
+  float m[G];     // the reference this pass takes probabilities against
+  float mtop[G];  // the largest exact max of a tile that broke the slack (or -inf)
+  float l[G];     // this lane's partial row sums (lanes l and l^32 are added at the end)
+  bool bad = false;  // some tile of this wave broke the slack in this pass
+  __device__ __forceinline__ PassSoftmax() {
 #pragma unroll
-    for (int kb = 0; kb < kBN / 32; ++kb)
-#pragma unroll
-      for (int r = (kb == 0 ? 2 : 0); r < 16; ++r) mt = fmaxf(mt, s[kb][r]);
-    return pair_max(mt) * c;
+    for (int g = 0; g < G; ++g) m[g] = mtop[g] = -__builtin_inff(), l[g] = 0.f;
   }
-
-  // Take a tile's scaled max into account: move m (and rescale O, l) only when the tile
-  // exceeds it by more than kRescaleLog2.  The branch is wave-uniform and rare.
-  __device__ __forceinline__ void apply_max(float mt, f32x16 (&o)[D / 32]) {
-    const bool need = mt > m + kRescaleLog2;
-    if (__builtin_amdgcn_ballot_w64(need) != 0) {
-      const float m_new = fmaxf(m, mt);
-      const float alpha = __builtin_amdgcn_exp2f(m - m_new);
-      m = m_new;
-      l *= alpha;
+  // The reference of the next pass (every score of row g is at or below it).
+  __device__ __forceinline__ void next_pass() {
 #pragma unroll
-      for (int db = 0; db < D / 32; ++db)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) o[db][r] *= alpha;
+    for (int g = 0; g < G; ++g) {
+      m[g] = fmaxf(m[g] + kSlackLog2, mtop[g]);
+      mtop[g] = -__builtin_inff();
+      l[g] = 0.f;
     }
+    bad = false;
   }
 };
 
+// Scaled row max of one 32-key score block (this lane's keys, then its partner lane's).
+__device__ __forceinline__ float row_max32(const f32x16& s, float c) {
+  float mt = fmaxf(s[0], s[1]);
+#pragma unroll
+  for (int r = 2; r < 16; ++r) mt = fmaxf(mt, s[r]);
+  return pair_max(mt) * c;
+}
+// The same for a 64-key tile (two blocks).
+__device__ __forceinline__ float row_max64(const f32x16 (&s)[2], float c) {
+  float mt = fmaxf(s[0][0], s[0][1]);
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+    for (int r = (kb == 0 ? 2 : 0); r < 16; ++r) mt = fmaxf(mt, s[kb][r]);
+  return pair_max(mt) * c;
+}
+
+// Does any wave of the workgroup need a second pass?  Every wave calls this after its
+// last tile load has landed; flags are four ints of LDS that no tile load writes.
+__device__ __forceinline__ bool workgroup_redo(volatile __attribute__((address_space(3))) int* flags, bool bad,
+                                               int wave, int lane) {
+  if (lane == 0) flags[wave] = bad ? 1 : 0;
+  __syncthreads();
+  const bool redo = (flags[0] | flags[1] | flags[2] | flags[3]) != 0;
+  __syncthreads();  // the flags are read before any wave can write them again
+  return redo;
+}
 
 // bf16 path with direct-to-LDS tiles.  At the top of iteration j the scores
-// S_j are in registers, the running max already covers them, and K_{j+1}, V_j
-// are in LDS.  Iteration j starts the DMA of K_{j+2} and V_{j+1} into the
-// buffers the previous iteration released, issues S_{j+1} = K_{j+1} Q^T on the
-// MFMA pipe while the exponentials of tile j run on the VALU, accumulates
-// O += V_j P_j while the VALU takes the row max of S_{j+1}, then waits for its
-// DMA and meets the other waves at the one barrier of the iteration.  Scores of a
-// tile that holds keys at or past the end are masked to -inf (a rare branch) before
-// its max is taken.  The loop runs an even number of iterations, so the last one or
+// S_j are in registers and K_{j+1}, V_j are in LDS.  Iteration j starts the DMA
+// of K_{j+2} and V_{j+1} into the buffers the previous iteration released,
+// issues S_{j+1} = K_{j+1} Q^T on the MFMA pipe while the exponentials of tile j
+// run on the VALU (against the pass's reference max, see PassSoftmax), checks
+// the tile's sums against the slack, accumulates O += V_j P_j, then waits for
+// its DMA and meets the other waves at the one barrier of the iteration.  Scores
+// of a tile that holds keys at or past the end are masked to -inf (a rare branch)
+// before their exponentials.  The loop runs an even number of iterations, so the last one or
 // two take phantom tiles past the end: their DMA zero-fills LDS without a memory
 // request and every score is masked, so they add p = 0.  The PV product of the last
 // real tile then needs no code of its own (a separate last-tile path made the
@@ -719,6 +746,7 @@ struct Softmax {
 // fences that keep the compiler from regrouping them.  At D = 256 (one wave
 // per SIMD) nothing else hides a stall; at D = 128 and 64 (two waves per SIMD)
 // the fixed order still measured 4-4.5% faster than the compiler's.
+//
 // Marks a branch whose body runs rarely (the last tile's mask, the slack check's max): an
 // empty volatile asm cannot be executed speculatively, so the compiler keeps the branch
 // instead of turning its body into selects computed on every iteration.
@@ -786,34 +814,16 @@ __device__ __forceinline__ void bf16_fwd_dma(const FwdArgs& a, char* smem_generi
         if (st_key(kb, r, hh) >= nv) sg[kb][r] = -__builtin_inff();
   };
 
-  P::template dma_tile<STREAM>(k_tile(0), kbuf0, wave_u, lane);
-  P::template dma_tile<STREAM>(v_tile(0), vbuf0, wave_u, lane);
-  P::template dma_tile<STREAM>(k_tile(1), kbuf1, wave_u, lane);
-  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's tile loads have landed in LDS
-  __syncthreads();
-  f32x16 s_cur[kBN / 32];
-  // S_0, with the loop's register form of the score MFMAs
-#pragma unroll
-  for (int kk = 0; kk < P::NQ; ++kk)
-#pragma unroll
-    for (int kb = 0; kb < kBN / 32; ++kb) {
-      const bf16x8 kf = P::k_frag(kbuf0, kbase, (kBN / 32) * kk + kb);
-      if (kk == 0) mfma_vgpr_first(s_cur[kb], kf, qf.v[0]);
-      else mfma_vgpr_acc(s_cur[kb], kf, qf.v[kk]);
-    }
-  asm volatile("s_nop 7\n\ts_nop 7" ::: "memory");  // XDL result -> VALU read (row_max below)
-  __syncthreads();  // every wave is done with K_0 before its buffer is refilled
-
+  volatile __attribute__((address_space(3))) int* const bad_flag =
+      (volatile __attribute__((address_space(3))) int*)(smem + P::FLAGS);  // one per wave
   f32x16 o[D / 32];
-#pragma unroll
-  for (int db = 0; db < D / 32; ++db) o[db] = f32x16{};
-  Softmax<D> sm;
+  PassSoftmax<1> sm;
   u32x4 pk[kBN / 16];
-  if (nv_of(0) < kBN) mask_scores(s_cur, nv_of(0));
-  sm.apply_max(Softmax<D>::row_max(s_cur, c), o);
+  // S_j and S_{j+1}, in two register sets used alternately, so that no MFMA of one
+  // iteration has to wait for the reads of the previous iteration's scores
+  f32x16 s_cur[kBN / 32], s_alt[kBN / 32];
 
-  // sc holds S_j; S_{j+1} is accumulated into sn (two register sets, used alternately, so that
-  // no MFMA of one iteration has to wait for the reads of the previous iteration's scores)
+  // sc holds S_j; S_{j+1} is accumulated into sn
   auto iteration = [&](int j, f32x16 (&sc)[kBN / 32], f32x16 (&sn)[kBN / 32]) {
     lds_char* const k_next = (j & 1) ? kbuf0 : kbuf1;  // K_{j+1}
     lds_char* const k_free = (j & 1) ? kbuf1 : kbuf0;  // K_j consumed -> K_{j+2}
@@ -825,11 +835,10 @@ __device__ __forceinline__ void bf16_fwd_dma(const FwdArgs& a, char* smem_generi
       constexpr int NS = P::NQ * (kBN / 32);     // QK^T MFMAs per tile
       constexpr int NV = (D / 32) * (kBN / 16);  // PV MFMAs per tile
       constexpr int EPS = (kBN / 2) / NS;        // softmax elements per QK^T slot
-      constexpr int MPS = (kBN / 2) / NV;        // max elements per PV slot
       bf16x8 kf[R], vf[R];
 #pragma unroll
       for (int i = 0; i < R; ++i) kf[i] = P::k_frag(k_next, kbase, i);
-      const float nm = -sm.m;
+      const float nm = -sm.m[0];
       float acc[4] = {0.f, 0.f, 0.f, 0.f};
       float pe[kBN / 2], xe[kBN / 2];
       __builtin_amdgcn_sched_barrier(0);
@@ -864,7 +873,15 @@ __device__ __forceinline__ void bf16_fwd_dma(const FwdArgs& a, char* smem_generi
         }
         __builtin_amdgcn_sched_barrier(0);
       }
-      sm.l += (acc[0] + acc[1]) + (acc[2] + acc[3]);
+      // the tile's sum; past the slack, record the tile's exact max (rare: the scores are
+      // still in sc) and mark the pass
+      const float sum = (acc[0] + acc[1]) + (acc[2] + acc[3]);
+      sm.l[0] += sum;
+      if (__builtin_amdgcn_ballot_w64(!(sum <= __builtin_exp2f(kSlackLog2))) != 0) {
+        rare_path();
+        sm.bad = true;
+        sm.mtop[0] = fmaxf(sm.mtop[0], row_max64(sc, c));
+      }
       // the scores were written by MFMAs the compiler does not see as such: keep the
       // VALU reads of S_{j+1} below clear of the last of them (16 wait states here,
       // on top of the two MFMA issues in between)
@@ -875,48 +892,65 @@ __device__ __forceinline__ void bf16_fwd_dma(const FwdArgs& a, char* smem_generi
         mask_scores(sn, nv_of(j + 1));
       }
       __builtin_amdgcn_sched_barrier(0);
-      float mx = -__builtin_inff();
 #pragma unroll
       for (int i = 0; i < NV; ++i) {
         const int ks = i / (D / 32), db = i % (D / 32);
         o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[i % R], __builtin_bit_cast(bf16x8, pk[ks]), o[db], 0, 0, 0);
         if (i + R < NV) vf[i % R] = P::v_frag(v_cur, vbase, i + R);
-#pragma unroll
-        for (int t = 0; t < MPS; ++t) {
-          const int e = i * MPS + t;
-          mx = fmaxf(mx, sn[e >> 4][e & 15]);
-        }
         __builtin_amdgcn_sched_barrier(0);
       }
-      sm.apply_max(pair_max(mx) * c, o);
     }
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this iteration's tile loads have landed
     lds_barrier();
   };
 
-  // iterations 0 .. T2 - 1, T2 = T rounded up to even: iteration j adds PV_j and takes the
-  // scores of tile j + 1 (phantom tiles at or past T are all masked)
-  f32x16 s_alt[kBN / 32];
+  // one pass over the keys; a second runs only if the first marked a row bad (see PassSoftmax)
   const int T2 = (T + 1) & ~1;
-  for (int j = 0; j < T2; j += 2) {
-    iteration(j, s_cur, s_alt);
-    iteration(j + 1, s_alt, s_cur);
-  }
-  __builtin_amdgcn_s_waitcnt(0x0F70);  // no tile load may still be writing LDS when the workgroup ends
+  for (int pass = 0;; ++pass) {
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db) o[db] = f32x16{};
+    P::template dma_tile<STREAM>(k_tile(0), kbuf0, wave_u, lane);
+    P::template dma_tile<STREAM>(v_tile(0), vbuf0, wave_u, lane);
+    P::template dma_tile<STREAM>(k_tile(1), kbuf1, wave_u, lane);
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's tile loads have landed in LDS
+    __syncthreads();
+    // S_0, with the loop's register form of the score MFMAs
+#pragma unroll
+    for (int kk = 0; kk < P::NQ; ++kk)
+#pragma unroll
+      for (int kb = 0; kb < kBN / 32; ++kb) {
+        const bf16x8 kf = P::k_frag(kbuf0, kbase, (kBN / 32) * kk + kb);
+        if (kk == 0) mfma_vgpr_first(s_cur[kb], kf, qf.v[0]);
+        else mfma_vgpr_acc(s_cur[kb], kf, qf.v[kk]);
+      }
+    asm volatile("s_nop 7\n\ts_nop 7" ::: "memory");  // XDL result -> VALU read (row max below)
+    __syncthreads();  // every wave is done with K_0 before its buffer is refilled
+    if (nv_of(0) < kBN) mask_scores(s_cur, nv_of(0));
+    if (pass == 0) sm.m[0] = row_max64(s_cur, c);  // the first tile's max is the first pass's reference
 
-  const float l = pair_sum(sm.l);
+    // iterations 0 .. T2 - 1, T2 = T rounded up to even: iteration j adds PV_j and takes the
+    // scores of tile j + 1 (phantom tiles at or past T are all masked)
+    for (int j = 0; j < T2; j += 2) {
+      iteration(j, s_cur, s_alt);
+      iteration(j + 1, s_alt, s_cur);
+    }
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // no tile load may still be writing LDS when the pass ends
+    if (!workgroup_redo(bad_flag, sm.bad, wave, lane) || pass > 0) break;
+    sm.next_pass();
+  }
+
+  const float l = pair_sum(sm.l[0]);
+  const float lse_nat = (sm.m[0] + __builtin_amdgcn_logf(l)) * kLn2;
   if constexpr (PARTIAL && STREAM) {
-    static_assert(4 * 32 * D * 4 <= P::LDS_BYTES, "four waves' partial rows fit the tile buffers");
+    static_assert(4 * 32 * D * 4 <= P::FLAGS, "four waves' partial rows fit the tile buffers");
     lds_barrier();  // every wave is done with the last V tile: the buffers take the partial rows
-    write_partial_staged<D>(a, w, o, 1.0f / l, (sm.m + __builtin_amdgcn_logf(l)) * kLn2, h_half,
-                            smem + wave * (32 * D * 4), lane);
+    write_partial_staged<D>(a, w, o, 1.0f / l, lse_nat, h_half, smem + wave * (32 * D * 4), lane);
   } else if constexpr (!PARTIAL) {
-    static_assert(4 * 32 * D * 2 <= P::LDS_BYTES, "four waves' output rows fit the tile buffers");
+    static_assert(4 * 32 * D * 2 <= P::FLAGS, "four waves' output rows fit the tile buffers");
     lds_barrier();  // every wave is done with the last V tile: the buffers take the output rows
-    write_out_staged<D>(a, w, o, 1.0f / l, (sm.m + __builtin_amdgcn_logf(l)) * kLn2, h_half,
-                        smem + wave * (32 * D * 2), lane);
+    write_out_staged<D>(a, w, o, 1.0f / l, lse_nat, h_half, smem + wave * (32 * D * 2), lane);
   } else {
-    write_rows<P, D, PARTIAL>(a, w, o, 1.0f / l, (sm.m + __builtin_amdgcn_logf(l)) * kLn2, h_half);
+    write_rows<P, D, PARTIAL>(a, w, o, 1.0f / l, lse_nat, h_half);
   }
 }
 
@@ -1014,14 +1048,6 @@ __device__ __forceinline__ Work next_group(const FwdArgs& a, Work w) {
   return w;
 }
 
-// Scaled row max of one 32-key score block (this lane's keys, then its partner lane's).
-__device__ __forceinline__ float row_max32(const f32x16& s, float c) {
-  float mt = fmaxf(s[0], s[1]);
-#pragma unroll
-  for (int r = 2; r < 16; ++r) mt = fmaxf(mt, s[r]);
-  return pair_max(mt) * c;
-}
-
 // XDL wait states before a VALU read of an O tile written by inline MFMAs: the tile is an
 // operand of the asm, so no read of it -- the compiler's own register copies included --
 // can be placed before the wait.
@@ -1034,28 +1060,6 @@ __device__ __forceinline__ void s_result_guard(f32x16& s0, f32x16& s1) {
   asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+v"(s0), "+v"(s1));
   __builtin_amdgcn_sched_barrier(0);
 }
-
-// Softmax state of one lane of the 64-row kernel: its two rows (groups 0 and 1).
-//
-// O is never rescaled inside the tile loop: with O in all 256 AGPRs, an in-place rescale
-// (rare as it is) would make the register allocator hold a second copy of an O tile,
-// which does not fit, and it would spill O in the hot loop.  Instead all probabilities of
-// a pass are taken against one reference per row: the first tile's (scaled) max.  No
-// per-tile max is taken: a tile is checked through its sums instead.  While a lane's sum
-// over a tile stays at or below 2^kWideSlackLog2, every p of it does too, so the tile's
-// scores are at most the reference + kWideSlackLog2, and the sums cannot overflow (a row
-// has fewer than 2^22 keys, so this holds for any V below 2^86).  A tile that breaks this
-// marks the pass bad and records its exact max; the workgroup then runs the pass again
-// against max(reference + kWideSlackLog2, recorded maxima), which every score of the row
-// is at or below.  O / l is the same softmax either way: only the common scale differs.
-constexpr float kWideSlackLog2 = 20.0f;
-
-struct WideSoftmax {
-  float m[2];     // the reference this pass takes probabilities against
-  float mtop[2];  // the largest exact max of a tile that broke the slack (or -inf)
-  float l[2] = {0.f, 0.f};
-  bool bad = false;  // some tile of this wave broke the slack in this pass
-};
 
 template <int D, bool PARTIAL, bool STREAM>
 __device__ __forceinline__ void bf16_fwd_wide(const FwdArgs& a, char* smem_generic) {
@@ -1134,9 +1138,7 @@ __device__ __forceinline__ void bf16_fwd_wide(const FwdArgs& a, char* smem_gener
   const int vbase = P::v_base(lane);
 
   f32x16 o[2][D / 32];
-  WideSoftmax sm;
-  sm.m[0] = sm.m[1] = -__builtin_inff();
-  sm.mtop[0] = sm.mtop[1] = -__builtin_inff();
+  PassSoftmax<2> sm;
   // Scores of the tile in flight: group 0 has one register block, group 1 two (s1a, s1b),
   // used in alternate iterations, so that group 1's exponentials of tile j run beside the
   // QK^T MFMAs of tile j + 1 while group 0's run beside the PV MFMAs: each phase carries
@@ -1176,7 +1178,7 @@ __device__ __forceinline__ void bf16_fwd_wide(const FwdArgs& a, char* smem_gener
   // record the tile's exact scaled max (rare; the scores are still in sg) and mark the pass.
   auto exp_end = [&](const f32x16& sg, int g, float acc) {
     sm.l[g] += acc;
-    if (__builtin_amdgcn_ballot_w64(!(acc <= __builtin_exp2f(kWideSlackLog2))) != 0) {
+    if (__builtin_amdgcn_ballot_w64(!(acc <= __builtin_exp2f(kSlackLog2))) != 0) {
       rare_path();
       sm.bad = true;
       sm.mtop[g] = fmaxf(sm.mtop[g], row_max32(sg, c));
@@ -1312,13 +1314,12 @@ __device__ __forceinline__ void bf16_fwd_wide(const FwdArgs& a, char* smem_gener
     }
   };
 
-  // one pass over the keys; a second runs only if the first marked a row bad (see WideSoftmax)
+  // one pass over the keys; a second runs only if the first marked a row bad (see PassSoftmax)
   for (int pass = 0;; ++pass) {
 #pragma unroll
     for (int g = 0; g < 2; ++g)
 #pragma unroll
       for (int db = 0; db < D / 32; ++db) o[g][db] = f32x16{};
-    sm.l[0] = sm.l[1] = 0.f;
     dma(k_tile(0), kb(0));
     dma(v_tile(0), vb(0));
     dma(k_tile(1), kb(1));
@@ -1366,15 +1367,8 @@ __device__ __forceinline__ void bf16_fwd_wide(const FwdArgs& a, char* smem_gener
       iteration(j + 1, std::true_type{}, s1b, s1a, p0b, p0a);
     }
     __builtin_amdgcn_s_waitcnt(0x0F70);  // no tile load may still be writing LDS when the pass ends
-    // does any wave of the workgroup need the second pass?
-    if (lane == 0) bad_flag[wave] = sm.bad ? 1 : 0;
-    __syncthreads();
-    const bool redo = (bad_flag[0] | bad_flag[1] | bad_flag[2] | bad_flag[3]) != 0;
-    __syncthreads();  // the flags are read before any wave can write them again
-    if (!redo || pass > 0) break;
-#pragma unroll
-    for (int g = 0; g < 2; ++g) sm.m[g] = fmaxf(sm.m[g] + kWideSlackLog2, sm.mtop[g]);
-    sm.bad = false;
+    if (!workgroup_redo(bad_flag, sm.bad, wave, lane) || pass > 0) break;
+    sm.next_pass();
   }
 
   // the output rows are recomputed here rather than kept in registers through the loop

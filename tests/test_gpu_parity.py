@@ -307,8 +307,8 @@ def test_scale_sign_and_zero(scale, fwd_rows):
 
 @pytest.mark.parametrize("D", [128, 256])
 def test_growing_scores_exercise_rescale(D):
-    """Key norms grow along the sequence, so the running max keeps moving past the lazy
-    rescale threshold and O is rescaled many times inside one row."""
+    """Key norms grow along the sequence, so every row's scores climb far past the max of its
+    first key tile, the reference its probabilities are first taken against."""
     B, H, Tq, S = 1, 2, 64, 2048
     g = torch.Generator(device=DEV).manual_seed(1400 + D)
     q = torch.randn(B, H, Tq, D, device=DEV, generator=g).abs().to(torch.bfloat16)
@@ -319,15 +319,15 @@ def test_growing_scores_exercise_rescale(D):
     scale = 1.0 / math.sqrt(D)
     out, lse = _run_fused(q, k, v, kv, scale)
     ro, rl = _oracle(q, k, v, kv, scale)
-    assert np.isfinite(rl).all() and rl.max() > 20.0  # scores grow far past the 2^8 rescale threshold
+    assert np.isfinite(rl).all() and rl.max() > 20.0  # scores grow far past the first tile's
     assert_parity(out, lse, ro, rl, "bf16", f"growing D={D}")
 
 
 @pytest.mark.parametrize("D", [128, 256])
 def test_score_jump_past_exp_overflow(D, fwd_rows):
     """One late key block scores more than 128 log2 units above everything before it, so a
-    probability taken against an earlier reference overflows fp32 (2^128): the 32-row kernel
-    must move its max before taking it, the 64-row kernel must redo the pass."""
+    probability taken against an earlier reference overflows fp32 (2^128): either kernel
+    must redo its pass against a reference at or above the jump."""
     _skip_dup(D, fwd_rows, 300)
     B, H, Tq, S = 1, 2, 300, 1500
     q, k, v, kv = make_inputs(B, H, Tq, S, D, [S], "bf16", 1.0, seed=1900 + D, device=DEV)
@@ -428,51 +428,52 @@ def test_wide_edge_matrix(Tq, D, monkeypatch):
 
 def _first_tile_margins_log2(q, k, n, scale):
     """Per row, the amount by which its max scaled score climbs above its max over the first
-    32 keys, in log2 units (the 64-row kernel redoes a pass past a slack of 20).  Past 128, a
-    probability taken against the first tile's max overflows fp32 (2^128), so a kernel that
-    skipped the second pass would return inf or NaN for that row."""
+    64 keys, in log2 units (the first tile of the 32-row kernel; the 64-row kernel's is the
+    first 32, from which the climb is at least as large).  Both kernels redo a pass past a
+    slack of 20.  Past 128, a probability taken against the first tile's max overflows fp32
+    (2^128), so a kernel that skipped the second pass would return inf or NaN for that row."""
     s = torch.einsum("bhtd,bhsd->bhts", q.double().cpu(), k[:, :, :n].double().cpu()) * scale / math.log(2.0)
-    return s.amax(-1) - s[..., :32].amax(-1)
+    return s.amax(-1) - s[..., :64].amax(-1)
 
 
-@pytest.mark.parametrize("D", [128, 256])
-def test_wide_growing_scores_take_second_pass(D, monkeypatch):
+@pytest.mark.parametrize("D", [64, 128, 256])
+def test_growing_scores_take_second_pass(D, fwd_rows):
     """Key norms grow along the sequence, so every row climbs more than 128 log2 units past its
     first tile's max (one pass against that reference would overflow fp32): the workgroups
     must redo their pass against a reference no score of the row exceeds."""
-    monkeypatch.setenv("ATTN_PREFIX_FWD_ROWS", "256")
+    _skip_dup(D, fwd_rows, 300)
     B, H, Tq, S = 1, 2, 300, 2048
     g = torch.Generator(device=DEV).manual_seed(1600)
     q = torch.randn(B, H, Tq, D, device=DEV, generator=g).abs().to(torch.bfloat16)
-    ramp = torch.linspace(0.0, 30.0, S, device=DEV).view(1, 1, S, 1)
+    ramp = torch.linspace(0.0, 30.0 * math.sqrt(256 / D), S, device=DEV).view(1, 1, S, 1)
     k = (torch.rand(B, H, S, D, device=DEV, generator=g) * ramp).to(torch.bfloat16)
     v = torch.randn(B, H, S, D, device=DEV, generator=g).to(torch.bfloat16)
     kv = torch.tensor([S], dtype=torch.int32, device=DEV)
     scale = 1.0 / math.sqrt(D)
     margins = _first_tile_margins_log2(q, k, S, scale)
-    log(f"wide growing D={D}: first-tile margins {margins.min().item():.0f}..{margins.max().item():.0f} log2 units")
+    log(f"growing D={D} rows={fwd_rows}: first-tile margins {margins.min().item():.0f}..{margins.max().item():.0f} log2 units")
     assert margins.min().item() > 128.0  # every row needs the second pass
     out, lse = _run_fused(q, k, v, kv, scale)
     ro, rl = _oracle(q, k, v, kv, scale)
-    assert_parity(out, lse, ro, rl, "bf16", f"wide growing D={D}")
+    assert_parity(out, lse, ro, rl, "bf16", f"growing D={D} rows={fwd_rows}")
 
 
-@pytest.mark.parametrize("D", [128, 256])
-def test_wide_one_row_takes_second_pass(D, monkeypatch):
+@pytest.mark.parametrize("D", [64, 128, 256])
+def test_one_row_takes_second_pass(D, fwd_rows):
     """One query row meets one late key more than 128 log2 units above everything before it
     (fp32 overflow against the first tile's max); the other rows of its workgroup do not,
     and every row must come out right after the redo."""
-    monkeypatch.setenv("ATTN_PREFIX_FWD_ROWS", "256")
+    _skip_dup(D, fwd_rows, 512)
     B, H, Tq, S = 1, 1, 512, 1000
     q, k, v, kv = make_inputs(B, H, Tq, S, D, [S], "bf16", 1.0, seed=1700, device=DEV)
     scale = 1.0 / math.sqrt(D)
-    k[0, 0, 900] = (q[0, 0, 37].float() * 10.0).to(torch.bfloat16)  # row 37 meets key 900
+    k[0, 0, 900] = (q[0, 0, 37].float() * 10.0 * math.sqrt(256 / D)).to(torch.bfloat16)  # row 37 meets key 900
     margin = _first_tile_margins_log2(q[:, :, 37:38], k, S, scale).max().item()
-    log(f"wide one row D={D}: first-tile margin {margin:.0f} log2 units")
+    log(f"one row D={D} rows={fwd_rows}: first-tile margin {margin:.0f} log2 units")
     assert margin > 128.0
     out, lse = _run_fused(q, k, v, kv, scale)
     ro, rl = _oracle(q, k, v, kv, scale)
-    assert_parity(out, lse, ro, rl, "bf16", f"wide one bad row D={D}")
+    assert_parity(out, lse, ro, rl, "bf16", f"one bad row D={D} rows={fwd_rows}")
 
 
 @pytest.mark.parametrize("Tq", [257, 300, 511, 700])
