@@ -151,7 +151,15 @@ void bwd_dq_slot_kernel(BwdArgs a) {
   P::load_q(qf, reinterpret_cast<const uint16_t*>(a.q) + src_row * D, row_ok, h_half);
   P::load_q(gf, reinterpret_cast<const uint16_t*>(a.dout) + src_row * D, row_ok, h_half);
   const float L = row_ok ? a.lse[grow] * kLog2e : 0.0f;
-  const float dl = row_ok ? a.delta[grow] : 0.0f;
+  // dP^T - delta is formed by the MFMAs: each dP^T chain starts from a block of -delta (all
+  // 16 registers of a lane belong to its query row), which spares a subtraction per element
+  f32x16 neg_dl;
+  {
+    const float dl = row_ok ? a.delta[grow] : 0.0f;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) neg_dl[e] = -dl;
+    asm volatile("" : "+v"(neg_dl));  // one live block, not rebuilt before every chain
+  }
   float c = a.scale_log2;
   if (c < 0.0f) {  // c * (q.k) == |c| * ((-q).k): keep c > 0 so that a -inf score gives p = 0
     c = -c;
@@ -193,7 +201,8 @@ void bwd_dq_slot_kernel(BwdArgs a) {
     f32x16 s[2], dp[2];
     u32x4 pk[4];
     float d8[8];
-    // slot j of phases A and B: MFMA j of half `hf`: j even -> S^T (A = K rows), odd -> dP^T (A = V rows)
+    // slot j of phases A and B: MFMA j of half `hf`: j even -> S^T (A = K rows), odd ->
+    // dP^T - delta (A = V rows)
     auto frag_ab = [&](int hf, int j) {
       const int kk = j >> 1;
       return P::k_frag((j & 1) ? vt : kt, kbase, 2 * kk + hf);
@@ -201,13 +210,17 @@ void bwd_dq_slot_kernel(BwdArgs a) {
     auto mfma_ab = [&](int hf, int j, bf16x8 fr) {
       const int kk = j >> 1;
       f32x16& d = (j & 1) ? dp[hf] : s[hf];
-      if (kk == 0) mfma_vgpr_first(d, fr, (j & 1) ? gf.v[0] : qf.v[0]);
-      else mfma_vgpr_acc(d, fr, (j & 1) ? gf.v[kk] : qf.v[kk]);
+      if (kk == 0) {
+        if (j & 1) mfma_vgpr_from(d, fr, gf.v[0], neg_dl);
+        else mfma_vgpr_first(d, fr, qf.v[0]);
+      } else {
+        mfma_vgpr_acc(d, fr, (j & 1) ? gf.v[kk] : qf.v[kk]);
+      }
     };
     // softmax element e (0..15) of half hf: register e of S^T block hf
     auto elem = [&](int hf, int e) {
       const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[hf][e], c, -L));
-      d8[e & 7] = p * (dp[hf][e] - dl);
+      d8[e & 7] = p * dp[hf][e];
       if ((e & 7) == 7)
         pk[2 * hf + (e >> 3)] = u32x4{pack_bf16x2(d8[0], d8[1]), pack_bf16x2(d8[2], d8[3]),
                                       pack_bf16x2(d8[4], d8[5]), pack_bf16x2(d8[6], d8[7])};
@@ -354,8 +367,9 @@ void bwd_dkdv_slot_kernel(BwdArgs a) {
     const __amdgpu_buffer_rsrc_t rs = make_rsrc((wave_u == 0 ? lse_bh : del_bh) + (int64_t)t * kBN, (uint32_t)valid * 4);
     return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rs, (uint32_t)lane * 4, 0, 0));
   };
+  // (delta is kept negated: the dP chains start from it, see below)
   auto stat_value = [&](int t, float raw) -> float {
-    if (wave_u != 0) return raw;
+    if (wave_u != 0) return -raw;
     return t * kBN + lane < a.Tq ? raw * kLog2e : __builtin_inff();
   };
 
@@ -392,30 +406,44 @@ void bwd_dkdv_slot_kernel(BwdArgs a) {
     f32x16 s[2], dp[2];
     u32x4 ppk[4], dpk[4];
     float p8[8], d8[8];
-    f32x4 Lq[2], Dq[2];  // statistics of four queries, a ring of two groups
+    f32x4 Lq[2];  // lse of four queries, a ring of two groups
     auto stat4 = [&](int g, int which) {  // group g of 4 queries: 8 g' + 4 h + i within half g / 4
       const int q0 = 32 * (g >> 2) + 8 * (g & 3) + 4 * h_half;
       return *reinterpret_cast<const f32x4*>(&stat[cur][which][q0]);
     };
+    // the -delta block of half hf in the register order of a dP block: each dP chain starts
+    // from it, so that it yields dP - delta
+    auto neg_delta16 = [&](int hf) {
+      f32x16 r;
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const f32x4 x = stat4(4 * hf + g, 1);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) r[4 * g + i] = x[i];
+      }
+      return r;
+    };
+    f32x16 nd = neg_delta16(0);
     auto frag_ab = [&](int hf, int j) {  // j even: S (A = Q rows), odd: dP (A = dO rows)
       return P::k_frag((j & 1) ? gt_ : qt_, kbase, 2 * (j >> 1) + hf);
     };
     auto mfma_ab = [&](int hf, int j, bf16x8 fr) {
       const int kk = j >> 1;
       f32x16& d = (j & 1) ? dp[hf] : s[hf];
-      if (kk == 0) mfma_vgpr_first(d, fr, (j & 1) ? vf.v[0] : kf.v[0]);
-      else mfma_vgpr_acc(d, fr, (j & 1) ? vf.v[kk] : kf.v[kk]);
+      if (kk == 0) {
+        if (j & 1) mfma_vgpr_from(d, fr, vf.v[0], nd);
+        else mfma_vgpr_first(d, fr, kf.v[0]);
+      } else {
+        mfma_vgpr_acc(d, fr, (j & 1) ? vf.v[kk] : kf.v[kk]);
+      }
     };
     // element e (0..15) of half hf: register e of block hf, query 32 hf + 8 (e / 4) + 4 h + e % 4
     auto elem = [&](int hf, int e) {
       const int g = 4 * hf + (e >> 2);
-      if ((e & 3) == 0 && (e >> 2) + 1 < 4) {  // fetch the next group of the same half
-        Lq[(g + 1) & 1] = stat4(g + 1, 0);
-        Dq[(g + 1) & 1] = stat4(g + 1, 1);
-      }
+      if ((e & 3) == 0 && (e >> 2) + 1 < 4) Lq[(g + 1) & 1] = stat4(g + 1, 0);  // the next group of the same half
       const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[hf][e], c, -Lq[g & 1][e & 3]));
       p8[e & 7] = p;
-      d8[e & 7] = p * (dp[hf][e] - Dq[g & 1][e & 3]);
+      d8[e & 7] = p * dp[hf][e];  // dp holds dP - delta
       if ((e & 7) == 7) {
         const int ks = 2 * hf + (e >> 3);
         ppk[ks] = u32x4{pack_bf16x2(p8[0], p8[1]), pack_bf16x2(p8[2], p8[3]), pack_bf16x2(p8[4], p8[5]),
@@ -440,7 +468,6 @@ void bwd_dkdv_slot_kernel(BwdArgs a) {
 #pragma unroll
     for (int i = 0; i < R; ++i) fr[i] = frag_ab(0, i);
     Lq[0] = stat4(0, 0);
-    Dq[0] = stat4(0, 1);
     __builtin_amdgcn_sched_barrier(0);
     // phase A: S, dP of queries 0..31, and the next tiles' DMA
 #pragma unroll
@@ -454,6 +481,7 @@ void bwd_dkdv_slot_kernel(BwdArgs a) {
       }
       __builtin_amdgcn_sched_barrier(0);
     }
+    nd = neg_delta16(1);  // for the dP chain of phase B
     xdl_result_guard();
     // phase B: S, dP of queries 32..63; P, dS of queries 0..31
 #pragma unroll
@@ -467,7 +495,6 @@ void bwd_dkdv_slot_kernel(BwdArgs a) {
       __builtin_amdgcn_sched_barrier(0);
     }
     Lq[0] = stat4(4, 0);  // group 4 opens the second half
-    Dq[0] = stat4(4, 1);
     xdl_result_guard();
     // phase C: dV, dK over queries 0..31; P, dS of queries 32..63
 #pragma unroll
@@ -579,8 +606,9 @@ void bwd_dkdv_pipe_kernel(BwdArgs a) {
     const __amdgpu_buffer_rsrc_t rs = make_rsrc((wave_u == 0 ? lse_bh : del_bh) + (int64_t)t * kBN, (uint32_t)valid * 4);
     return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rs, (uint32_t)lane * 4, 0, 0));
   };
+  // (delta is kept negated: the dP chains start from it, see below)
   auto stat_value = [&](int t, float raw) -> float {
-    if (wave_u != 0) return raw;
+    if (wave_u != 0) return -raw;
     return t * kBN + lane < a.Tq ? raw * kLog2e : __builtin_inff();
   };
 
@@ -614,10 +642,30 @@ void bwd_dkdv_pipe_kernel(BwdArgs a) {
   }
   __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
   __syncthreads();
+  // -delta of the four queries of group g (0..7) of a tile's statistics buffer: softmax
+  // element e is register e % 16 of block e / 16, query 32 (e / 16) + 8 ((e % 16) / 4) + 4 h + e % 4
+  auto neg_delta4 = [&](int buf, int g) {
+    const int q0 = 32 * (g >> 2) + 8 * (g & 3) + 4 * h_half;
+    return *reinterpret_cast<const f32x4*>(&stat[buf][1][q0]);
+  };
+  // the -delta block of query block kb (32 queries) of buffer buf, in the register order of
+  // a dP block, so that a dP chain starting from it yields dP - delta
+  auto neg_delta16 = [&](int buf, int kb) {
+    f32x16 r;
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const f32x4 x = neg_delta4(buf, 4 * kb + g);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) r[4 * g + i] = x[i];
+    }
+    return r;
+  };
   f32x16 s0[kBN / 32], d0[kBN / 32], s1[kBN / 32], d1[kBN / 32];
   P::scores_vgpr(s0, kf, qb_(0), kbase);
   P::scores_vgpr(d0, vf, gb_(0), kbase);
   xdl_result_guard();
+#pragma unroll
+  for (int kb = 0; kb < kBN / 32; ++kb) d0[kb] += neg_delta16(0, kb);  // tile 0: dP_0 - delta once here
 
   auto iteration = [&](int t, f32x16 (&sc)[kBN / 32], f32x16 (&dc)[kBN / 32], f32x16 (&sn)[kBN / 32],
                        f32x16 (&dn)[kBN / 32]) {
@@ -630,9 +678,11 @@ void bwd_dkdv_pipe_kernel(BwdArgs a) {
       const int q0 = 32 * (g >> 2) + 8 * (g & 3) + 4 * h_half;
       return *reinterpret_cast<const f32x4*>(&stat[bc][which][q0]);
     };
-    f32x4 Lq[2], Dq[2];  // groups g and g + 1 (ring of two)
+    f32x4 Lq[2];  // groups g and g + 1 (ring of two)
     Lq[0] = stat4(0, 0);
-    Dq[0] = stat4(0, 1);
+    // dP_{t+1} - delta: each chain of the next tile's dP starts from its block of -delta
+    f32x16 nd[kBN / 32];
+    nd[0] = neg_delta16(bn, 0);
     u32x4 ppk[kBN / 16], dpk[kBN / 16];
     float pe[NE], de[NE];
     bf16x8 fr[R];
@@ -645,8 +695,13 @@ void bwd_dkdv_pipe_kernel(BwdArgs a) {
       {
         const int j = i >> 1, kb = j & 1, kk = j >> 1;
         f32x16& acc = (i & 1) ? dn[kb] : sn[kb];
-        if (kk == 0) mfma_vgpr_first(acc, fr[i % R], (i & 1) ? vf.v[0] : kf.v[0]);
-        else mfma_vgpr_acc(acc, fr[i % R], (i & 1) ? vf.v[kk] : kf.v[kk]);
+        if (kk == 0) {
+          if (i & 1) mfma_vgpr_from(acc, fr[i % R], vf.v[0], nd[kb]);
+          else mfma_vgpr_first(acc, fr[i % R], kf.v[0]);
+        } else {
+          mfma_vgpr_acc(acc, fr[i % R], (i & 1) ? vf.v[kk] : kf.v[kk]);
+        }
+        if (i == 0) nd[1] = neg_delta16(bn, 1);  // for slot 3
         if (i + R < NA) {
           const int ii = i + R;
           fr[i % R] = P::k_frag((ii & 1) ? gb_(bn) : qb_(bn), kbase, ii >> 1);
@@ -665,13 +720,10 @@ void bwd_dkdv_pipe_kernel(BwdArgs a) {
         const int e = i * EPS + u;
         if (e < NE) {
           const int kb = e >> 4, r = e & 15, g = e >> 2;
-          if ((e & 3) == 0 && g + 1 < NE / 4) {  // fetch the next group's statistics
-            Lq[(g + 1) & 1] = stat4(g + 1, 0);
-            Dq[(g + 1) & 1] = stat4(g + 1, 1);
-          }
+          if ((e & 3) == 0 && g + 1 < NE / 4) Lq[(g + 1) & 1] = stat4(g + 1, 0);  // the next group's lse
           const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[kb][r], c, -Lq[g & 1][e & 3]));
           pe[e] = p;
-          de[e] = p * (dc[kb][r] - Dq[g & 1][e & 3]);
+          de[e] = p * dc[kb][r];  // dc holds dP - delta
           if (e & 1) {
             ppk[e >> 3][(e & 7) >> 1] = pack_bf16x2(pe[e - 1], p);
             dpk[e >> 3][(e & 7) >> 1] = pack_bf16x2(de[e - 1], de[e]);

@@ -115,6 +115,11 @@ __device__ __forceinline__ void mfma_vgpr_first(f32x16& d, bf16x8 a, bf16x8 b) {
 __device__ __forceinline__ void mfma_vgpr_acc(f32x16& d, bf16x8 a, bf16x8 b) {
   asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(d) : "v"(a), "v"(b));
 }
+// The first MFMA of a chain that starts from a register block c instead of 0 (c is only
+// read, so one block can start many chains).
+__device__ __forceinline__ void mfma_vgpr_from(f32x16& d, bf16x8 a, bf16x8 b, const f32x16& c) {
+  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %3" : "=&v"(d) : "v"(a), "v"(b), "v"(c));
+}
 
 // O^T accumulation for the 64-rows-per-wave kernel (whose register file is full at
 // D = 256): the accumulator is kept in AGPRs and the operands in VGPRs by the constraints,
