@@ -4,10 +4,13 @@
 // workgroup, softmax attention over the key range [lo, hi) where hi <= n_b =
 // kv_len[b]: keys at or past n_b are never loaded (their LDS rows are zero
 // filled and their scores forced to -inf), which is the prefix-mask /
-// k-v-truncation identity of tabfm PR #80 (section Fix).  The softmax is the
-// fp32 online (running max / running sum) form, and partials over key chunks
-// carry a natural-log LSE so that they can be merged exactly (tabfm PR #81,
-// section Sequence-parallel inference).
+// k-v-truncation identity of tabfm PR #80 (section Fix).  The softmax is an
+// fp32 online form with a running sum: the bf16 kernels take a pass's
+// probabilities against one reference max per row and run the pass again in
+// the rare case that a tile climbs too far past it (PassSoftmax); the fp32
+// path moves a running max every tile.  Partials over key chunks carry a
+// natural-log LSE so that they can be merged exactly (tabfm PR #81, section
+// Sequence-parallel inference).
 //
 // Wave layout (4 waves, 256 threads; each wave owns 32 query rows).  The two
 // contractions are issued transposed so that one lane owns one query row:

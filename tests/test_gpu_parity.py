@@ -345,6 +345,41 @@ def test_score_jump_past_exp_overflow(D, fwd_rows):
     assert_parity(out, lse, ro, rl, "bf16", f"score jump D={D}")
 
 
+@pytest.mark.parametrize("D", [64, 128, 256])
+@pytest.mark.parametrize("Tq", [100, 300])
+def test_splitkv_score_jump_redoes_the_chunk(D, Tq):
+    """A key block 128+ log2 units above everything before it sits inside a later chunk, past
+    that chunk's first tile: the partial kernel must redo that chunk's pass (a probability taken
+    against the chunk's first-tile max would overflow fp32), in the partial launch, its
+    streaming form (T_q <= 128) and the single launch, and the merge must still give the
+    oracle's result."""
+    B, H, S, chunk = 2, 2, 2000, 512
+    lens = [2000, 1500]
+    q, k, v, kv = make_inputs(B, H, Tq, S, D, lens, "bf16", 1.0, seed=1950 + D + Tq, device=DEV)
+    scale = 1.0 / math.sqrt(D)
+    qm = q.float().mean(dim=2, keepdim=True)
+    k[:, :, 1300:1364] = (qm / qm.norm(dim=-1, keepdim=True) * 40.0 * math.sqrt(D)).to(torch.bfloat16)
+    s = torch.einsum("bhtd,bhsd->bhts", q.double().cpu(), k.double().cpu()) * scale / math.log(2.0)
+    # the largest climb of any row of each (b, h), the smallest of those over (b, h)
+    jump = (s[..., 1300:1364].amax(-1) - s[..., 1024:1088].amax(-1)).amax(-1).min().item()
+    log(f"split score jump D={D} Tq={Tq}: {jump:.0f} log2 units over the chunk's first tile")
+    assert jump > 128.0, jump
+    ro, rl = ref_prefix_fwd(_np(q), _np(k), _np(v), np.array(lens), scale)
+    po, pl = _lib.attn_splitkv_partial(q, k, v, kv, chunk, scale)
+    out, lse = _lib.attn_lse_combine(po, pl, q.dtype)
+    torch.cuda.synchronize()
+    assert torch.isfinite(po).all() and torch.isfinite(out.float()).all()
+    assert_parity(out, lse, ro, rl, "bf16", f"split score jump D={D} Tq={Tq}")
+    _, rpl = ref_splitkv_partial(_np(q), _np(k), _np(v), np.array(lens), scale, chunk)
+    gpl = pl.cpu().double().numpy()
+    fin = np.isfinite(rpl)
+    assert np.array_equal(np.isfinite(gpl), fin)  # the empty chunk is -inf on both
+    assert np.abs(gpl[fin] - rpl[fin]).max() < 1e-3  # chunk 2 of both elements took the redo
+    o1, l1 = _lib.attn_splitkv_fwd(q, k, v, kv, chunk, scale)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, out) and torch.equal(l1, lse), "single launch differs from partial + combine"
+
+
 @pytest.mark.timeout(900)
 def test_largest_key_slice(fwd_rows):
     """One (b, h) key slice just under the 2^31-byte limit (D=256 bf16, S = 2^22 - 64):

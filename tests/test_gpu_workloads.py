@@ -40,8 +40,8 @@ def test_fused_workload_sampled_rows(name, rows):
 def test_fused_workload_sharp_sampled_rows(name, rows):
     """The ICL workloads at full size with q scaled by 4 (exact in bf16): scores spread 4x
     wider, so attention concentrates on a few hundred to a few thousand keys and the outputs
-    grow from ~2e-3 rms (where the 2e-2 max-abs bound says nothing) to 1-4e-2; the max moves
-    and rescales far more often.  Same launch as the benchmark."""
+    grow from ~2e-3 rms (where the 2e-2 max-abs bound says nothing) to 1-4e-2; the scores also
+    spread further from each row's first-tile reference max.  Same launch as the benchmark."""
     w = WORKLOADS[name]
     lens = w.lens()
     log(f"workload {name} (q x 4): B={w.B} H={w.H} D={w.D} Tq={w.Tq} S={w.S} kv_len={lens.tolist()}")
