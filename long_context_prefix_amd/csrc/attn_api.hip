@@ -126,6 +126,21 @@ attn_status_t launch_fwd_wide(FwdArgs a, int B, int H, hipStream_t stream, const
   return hipGetLastError() == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
 }
 
+// The 32-row kernel with eight waves (256 query rows) per workgroup; bf16, D = 128 or 64,
+// fused forward.
+template <int D>
+attn_status_t launch_fwd_8waves(FwdArgs a, int B, int H, hipStream_t stream) {
+  a.n_qtiles = (a.Tq + kBM8 - 1) / kBM8;
+  const int64_t grid = (int64_t)a.n_qtiles * B * H;
+  if (verbose())
+    fprintf(stderr, "[attn_prefix] prefix_fwd D=%d bf16 8 waves grid=%lld block=%d lds=%d\n", D, (long long)grid,
+            8 * 64, dma_kernel_lds_bytes<D, 8>());
+  (void)hipGetLastError();
+  hipLaunchKernelGGL((attn_fwd_kernel<Bf16Dma<D>, D, false, 2, false, false, 8>), dim3((unsigned)grid), dim3(8 * 64),
+                     0, stream, a);
+  return hipGetLastError() == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
+}
+
 // Compute units of the current device (cached per device; 256 if the query fails).
 int device_cus() {
   static std::atomic<int> cached[64];  // zero-initialized: not yet queried
@@ -149,17 +164,34 @@ int device_cus() {
 // on the 64-row path).  At D = 128 the 64-row kernel is as fast as the 32-row one, not
 // faster (its MFMAs wait on the softmax VALU work, which at D = 128 is twice as dense per
 // MFMA), so it runs only when ATTN_PREFIX_FWD_ROWS=256 forces it.
+//
+// At D = 128 and 64 the 32-row kernel also comes with eight waves per workgroup (256 rows,
+// one workgroup per CU; its tiles are loaded once per 256 rows and it waits and meets at a
+// barrier every other tile), with the same bits.  At D = 128 it measured 1.5-2 % faster
+// at ragged_32k and is taken when its workgroups fill at least one round of the CUs and
+// need no more rounds than the four-wave ones (two per CU); at D = 64 it measured 0.4 %
+// slower and runs only when forced.  ATTN_PREFIX_FWD_ROWS=128x8 forces it, =128 the
+// four-wave form.
 struct FwdPlan {
-  int kind;        // 0: 32-row kernel, 1: 64-row kernel, 2: mixed
+  int kind;        // 0: 32-row kernel, 1: 64-row kernel, 2: mixed, 3: 32-row kernel, 8 waves
   int wide_tiles;  // mixed: 256-row tiles per head on the 64-row path
 };
 
 FwdPlan plan_fwd(int D, attn_dtype_t dtype, int B, int H, int Tq) {
   FwdPlan p{0, 0};
-  if (dtype != ATTN_BF16 || (D != 256 && D != 128)) return p;
+  if (dtype != ATTN_BF16) return p;
   const char* e = getenv("ATTN_PREFIX_FWD_ROWS");
-  if (D == 128) return (e && strcmp(e, "256") == 0) ? FwdPlan{1, 0} : p;
   const int64_t heads = (int64_t)B * H;
+  if (D <= 128) {
+    if (e && strcmp(e, "128") == 0) return p;
+    if (e && strcmp(e, "128x8") == 0) return FwdPlan{3, 0};
+    if (D == 128 && e && strcmp(e, "256") == 0) return FwdPlan{1, 0};
+    if (D == 64) return p;
+    const int64_t cus = device_cus();
+    const int64_t wg8 = heads * ((Tq + kBM8 - 1) / kBM8), wg4 = heads * ((Tq + kBM - 1) / kBM);
+    const bool fills = wg8 >= cus && (wg8 + cus - 1) / cus <= (wg4 + 2 * cus - 1) / (2 * cus);
+    return fills ? FwdPlan{3, 0} : p;
+  }
   const int64_t full_w = Tq / kBMW;  // full 256-row tiles per head
   if (e && strcmp(e, "128") == 0) return p;
   if (e && strcmp(e, "256") == 0) return FwdPlan{1, 0};
@@ -405,6 +437,9 @@ attn_status_t attn_prefix_fwd(const void* q, const void* k, const void* v, const
     return D == 128 ? launch_fwd_wide<128, false>(a, B, H, reinterpret_cast<hipStream_t>(stream), "prefix_fwd")
                     : launch_fwd_wide<256, false>(a, B, H, reinterpret_cast<hipStream_t>(stream), "prefix_fwd");
   if (plan.kind == 2) return launch_fwd_mixed(a, B, H, plan.wide_tiles, reinterpret_cast<hipStream_t>(stream));
+  if (plan.kind == 3)
+    return D == 128 ? launch_fwd_8waves<128>(a, B, H, reinterpret_cast<hipStream_t>(stream))
+                    : launch_fwd_8waves<64>(a, B, H, reinterpret_cast<hipStream_t>(stream));
   const int64_t grid = (int64_t)a.n_qtiles * B * H;
   return dispatch_fwd<false>(a, D, dtype, grid, reinterpret_cast<hipStream_t>(stream));
 }

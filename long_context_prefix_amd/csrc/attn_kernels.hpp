@@ -49,6 +49,7 @@ typedef __attribute__((address_space(3))) char lds_char;
 
 constexpr int kThreads = 256;  // 4 wavefronts of 64
 constexpr int kBM = 128;       // query rows per workgroup (32 per wave)
+constexpr int kBM8 = 256;      // the same with eight waves (see bf16_fwd_dma)
 constexpr int kBN = 64;        // keys per tile
 constexpr float kLn2 = 0.693147180559945309f;
 constexpr float kLog2e = 1.442695040888963407f;
@@ -212,9 +213,10 @@ struct Bf16Dma {
     }
   }
 
-  // Issue this wave's share of one tile's DMA (blocks wave, wave+4, ...).  The resource
-  // covers only the tile's valid rows; other lanes write zeros without a fetch.
-  static constexpr int DMA_PER_WAVE = NBLK / 4;  // blocks of one tile each wave copies
+  // Issue this wave's share of one tile's DMA (blocks wave, wave + NW, ... of a workgroup of
+  // NW waves).  The resource covers only the tile's valid rows; other lanes write zeros
+  // without a fetch.
+  static constexpr int DMA_PER_WAVE = NBLK / 4;  // blocks of one tile each of four waves copies
 
   // One block (the bi-th of this wave's share) of a tile.  Issued as inline asm on
   // purpose: the compiler cannot tell which LDS bytes a direct-to-LDS load writes,
@@ -228,10 +230,10 @@ struct Bf16Dma {
   // STREAM marks the loads non-temporal, for launches in which every tile is read by
   // one workgroup only (one query tile per head): measured 2.5% faster there, and
   // 6.5% slower where many workgroups re-read the same tiles from L2.
-  template <bool STREAM = false>
+  template <bool STREAM = false, int NW = 4>
   __device__ static void dma_block(__amdgpu_buffer_rsrc_t rs, lds_char* buf, int wave_u, int lane, int bi) {
     const int r = lane / LPR, ch = lane % LPR;
-    const int b = wave_u + 4 * bi;
+    const int b = wave_u + NW * bi;
     const int j = key_of(b, r);
     const uint32_t lds = (uint32_t)(uintptr_t)(buf + b * BLK);
     const uint32_t voff = (uint32_t)(j * ROWB + ch * 16);
@@ -245,10 +247,10 @@ struct Bf16Dma {
                    : "m0");
   }
 
-  template <bool STREAM = false>
+  template <bool STREAM = false, int NW = 4>
   __device__ static void dma_tile(__amdgpu_buffer_rsrc_t rs, lds_char* buf, int wave_u, int lane) {
 #pragma unroll
-    for (int bi = 0; bi < DMA_PER_WAVE; ++bi) dma_block<STREAM>(rs, buf, wave_u, lane, bi);
+    for (int bi = 0; bi < NBLK / NW; ++bi) dma_block<STREAM, NW>(rs, buf, wave_u, lane, bi);
   }
 
   // per-lane base of the QK^T operand read (key i = lane % 32 of block kb = 0, chunk h)
@@ -722,13 +724,17 @@ __device__ __forceinline__ float row_max64(const f32x16 (&s)[2], float c) {
   return pair_max(mt) * c;
 }
 
-// Does any wave of the workgroup need a second pass?  Every wave calls this after its
-// last tile load has landed; flags are four ints of LDS that no tile load writes.
+// Does any of the NW waves of the workgroup need a second pass?  Every wave calls this
+// after its last tile load has landed; flags are NW ints of LDS that no tile load writes.
+template <int NW = 4>
 __device__ __forceinline__ bool workgroup_redo(volatile __attribute__((address_space(3))) int* flags, bool bad,
                                                int wave, int lane) {
   if (lane == 0) flags[wave] = bad ? 1 : 0;
   __syncthreads();
-  const bool redo = (flags[0] | flags[1] | flags[2] | flags[3]) != 0;
+  int any = 0;
+#pragma unroll
+  for (int i = 0; i < NW; ++i) any |= flags[i];
+  const bool redo = any != 0;
   __syncthreads();  // the flags are read before any wave can write them again
   return redo;
 }
@@ -755,6 +761,13 @@ __device__ __forceinline__ bool workgroup_redo(volatile __attribute__((address_s
 // per SIMD) nothing else hides a stall; at D = 128 and 64 (two waves per SIMD)
 // the fixed order still measured 4-4.5% faster than the compiler's.
 //
+// NW = 8 runs the same per-wave code with eight waves (256 query rows) per workgroup, one
+// workgroup per CU at two waves per SIMD (D = 128 and 64, fused forward only): every tile
+// is loaded once for 256 rows instead of once per 128-row workgroup, each wave issues half
+// the DMA, and the LDS left free holds four buffers of K and of V instead of two, so a
+// tile load has two iterations to land and only every other iteration ends with the wait
+// and the barrier.  Its output bits are those of NW = 4; at D = 128 it is 1.5-2 % faster.
+//
 // Marks a branch whose body runs rarely (the last tile's mask, the slack check's max): an
 // empty volatile asm cannot be executed speculatively, so the compiler keeps the branch
 // instead of turning its body into selects computed on every iteration.
@@ -762,20 +775,30 @@ __device__ __forceinline__ void rare_path() { asm volatile(""); }
 
 constexpr int kRing = 2;  // LDS operand reads issued this many slots ahead (2..4 measure the same)
 
-template <int D, bool PARTIAL, bool STREAM>
+// LDS of the 32-row kernel with NW waves: K and V in two (NW = 4) or four (NW = 8) buffers
+// each, then one second-pass flag per wave.
+template <int D, int NW>
+constexpr int dma_kernel_lds_bytes() {
+  return 2 * (NW == 8 ? 4 : 2) * Bf16Dma<D>::TILE_BYTES + NW * 4;
+}
+
+template <int D, bool PARTIAL, bool STREAM, int NW = 4>
 __device__ __forceinline__ void bf16_fwd_dma(const FwdArgs& a, char* smem_generic) {
   using P = Bf16Dma<D>;
+  static_assert(NW == 4 || (NW == 8 && !PARTIAL && D <= 128), "eight waves: fused forward at D <= 128");
+  constexpr int NB = NW == 8 ? 4 : 2;   // LDS buffers of K and of V
+  constexpr int DPW = P::NBLK / NW;     // DMA blocks of one tile per wave
+  constexpr int KA = NB == 2 ? 2 : 3;   // iteration j loads K_{j+KA} ...
+  constexpr int VA = KA - 1;            // ... and V_{j+VA}
   lds_char* const smem = (lds_char*)smem_generic;
-  lds_char* const kbuf0 = smem;
-  lds_char* const kbuf1 = smem + P::TILE_BYTES;
-  lds_char* const vbuf0 = smem + 2 * P::TILE_BYTES;
-  lds_char* const vbuf1 = smem + 3 * P::TILE_BYTES;
+  auto kbuf = [&](int m) { return smem + (m & (NB - 1)) * P::TILE_BYTES; };
+  auto vbuf = [&](int m) { return smem + (NB + (m & (NB - 1))) * P::TILE_BYTES; };
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int wave_u = __builtin_amdgcn_readfirstlane(wave);
   const int h_half = lane >> 5;
-  const Work w = decode<PARTIAL>(a, kBM, wave * 32 + (lane & 31));
+  const Work w = decode<PARTIAL>(a, 32 * NW, wave * 32 + (lane & 31));
   if (w.hi <= w.lo) {
     write_empty<P, D, PARTIAL>(a, w, h_half);
     return;
@@ -823,7 +846,7 @@ __device__ __forceinline__ void bf16_fwd_dma(const FwdArgs& a, char* smem_generi
   };
 
   volatile __attribute__((address_space(3))) int* const bad_flag =
-      (volatile __attribute__((address_space(3))) int*)(smem + P::FLAGS);  // one per wave
+      (volatile __attribute__((address_space(3))) int*)(smem + 2 * NB * P::TILE_BYTES);  // one per wave
   f32x16 o[D / 32];
   PassSoftmax<1> sm;
   u32x4 pk[kBN / 16];
@@ -831,13 +854,18 @@ __device__ __forceinline__ void bf16_fwd_dma(const FwdArgs& a, char* smem_generi
   // iteration has to wait for the reads of the previous iteration's scores
   f32x16 s_cur[kBN / 32], s_alt[kBN / 32];
 
-  // sc holds S_j; S_{j+1} is accumulated into sn
-  auto iteration = [&](int j, f32x16 (&sc)[kBN / 32], f32x16 (&sn)[kBN / 32]) {
-    lds_char* const k_next = (j & 1) ? kbuf0 : kbuf1;  // K_{j+1}
-    lds_char* const k_free = (j & 1) ? kbuf1 : kbuf0;  // K_j consumed -> K_{j+2}
-    lds_char* const v_cur = (j & 1) ? vbuf1 : vbuf0;   // V_j
-    lds_char* const v_free = (j & 1) ? vbuf0 : vbuf1;  // V_{j-1} consumed -> V_{j+1}
-    const __amdgpu_buffer_rsrc_t k_rs = k_tile(j + 2), v_rs = v_tile(j + 1);
+  // sc holds S_j; S_{j+1} is accumulated into sn.  Iteration j reads K_{j+1} and V_j and
+  // loads K_{j+KA} and V_{j+VA} into the buffers of K_{j+KA-NB} and V_{j+VA-NB}, which an
+  // earlier iteration read last, before a barrier.  With two buffers every iteration ends
+  // with the wait for its loads and the barrier; with four only odd iterations do, and the
+  // loads of iterations 2p and 2p + 1 are read by iterations 2p + 2 and 2p + 3.
+  auto iteration = [&](int j, f32x16 (&sc)[kBN / 32], f32x16 (&sn)[kBN / 32], auto odd_tag) {
+    constexpr bool odd = decltype(odd_tag)::value;  // j is odd
+    lds_char* const k_next = kbuf(j + 1);
+    lds_char* const v_cur = vbuf(j);
+    lds_char* const k_free = kbuf(j + KA);
+    lds_char* const v_free = vbuf(j + VA);
+    const __amdgpu_buffer_rsrc_t k_rs = k_tile(j + KA), v_rs = v_tile(j + VA);
     {
       constexpr int R = kRing;
       constexpr int NS = P::NQ * (kBN / 32);     // QK^T MFMAs per tile
@@ -859,9 +887,9 @@ __device__ __forceinline__ void bf16_fwd_dma(const FwdArgs& a, char* smem_generi
         if (i >= NS - R) vf[i - (NS - R)] = P::v_frag(v_cur, vbase, i - (NS - R));
         // the tile DMA is spread one block per slot over the first QK^T slots: all of it at
         // once would hold this wave's in-order issue (and the MFMA pipe) behind the loads
-        if (i < 2 * P::DMA_PER_WAVE) {
-          if (i < P::DMA_PER_WAVE) P::template dma_block<STREAM>(k_rs, k_free, wave_u, lane, i);
-          else P::template dma_block<STREAM>(v_rs, v_free, wave_u, lane, i - P::DMA_PER_WAVE);
+        if (i < 2 * DPW) {
+          if (i < DPW) P::template dma_block<STREAM, NW>(k_rs, k_free, wave_u, lane, i);
+          else P::template dma_block<STREAM, NW>(v_rs, v_free, wave_u, lane, i - DPW);
         }
 #pragma unroll
         for (int t = 0; t < EPS; ++t) {
@@ -908,8 +936,10 @@ __device__ __forceinline__ void bf16_fwd_dma(const FwdArgs& a, char* smem_generi
         __builtin_amdgcn_sched_barrier(0);
       }
     }
-    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this iteration's tile loads have landed
-    lds_barrier();
+    if (NB == 2 || odd) {
+      __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's tile loads so far have landed
+      lds_barrier();
+    }
   };
 
   // one pass over the keys; a second runs only if the first marked a row bad (see PassSoftmax)
@@ -917,9 +947,13 @@ __device__ __forceinline__ void bf16_fwd_dma(const FwdArgs& a, char* smem_generi
   for (int pass = 0;; ++pass) {
 #pragma unroll
     for (int db = 0; db < D / 32; ++db) o[db] = f32x16{};
-    P::template dma_tile<STREAM>(k_tile(0), kbuf0, wave_u, lane);
-    P::template dma_tile<STREAM>(v_tile(0), vbuf0, wave_u, lane);
-    P::template dma_tile<STREAM>(k_tile(1), kbuf1, wave_u, lane);
+    P::template dma_tile<STREAM, NW>(k_tile(0), kbuf(0), wave_u, lane);
+    P::template dma_tile<STREAM, NW>(v_tile(0), vbuf(0), wave_u, lane);
+    P::template dma_tile<STREAM, NW>(k_tile(1), kbuf(1), wave_u, lane);
+    if constexpr (NB == 4) {  // the first pair of iterations reads K_1, K_2, V_0 and V_1
+      P::template dma_tile<STREAM, NW>(k_tile(2), kbuf(2), wave_u, lane);
+      P::template dma_tile<STREAM, NW>(v_tile(1), vbuf(1), wave_u, lane);
+    }
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's tile loads have landed in LDS
     __syncthreads();
     // S_0, with the loop's register form of the score MFMAs
@@ -927,7 +961,7 @@ __device__ __forceinline__ void bf16_fwd_dma(const FwdArgs& a, char* smem_generi
     for (int kk = 0; kk < P::NQ; ++kk)
 #pragma unroll
       for (int kb = 0; kb < kBN / 32; ++kb) {
-        const bf16x8 kf = P::k_frag(kbuf0, kbase, (kBN / 32) * kk + kb);
+        const bf16x8 kf = P::k_frag(kbuf(0), kbase, (kBN / 32) * kk + kb);
         if (kk == 0) mfma_vgpr_first(s_cur[kb], kf, qf.v[0]);
         else mfma_vgpr_acc(s_cur[kb], kf, qf.v[kk]);
       }
@@ -939,11 +973,11 @@ __device__ __forceinline__ void bf16_fwd_dma(const FwdArgs& a, char* smem_generi
     // iterations 0 .. T2 - 1, T2 = T rounded up to even: iteration j adds PV_j and takes the
     // scores of tile j + 1 (phantom tiles at or past T are all masked)
     for (int j = 0; j < T2; j += 2) {
-      iteration(j, s_cur, s_alt);
-      iteration(j + 1, s_alt, s_cur);
+      iteration(j, s_cur, s_alt, std::false_type{});
+      iteration(j + 1, s_alt, s_cur, std::true_type{});
     }
     __builtin_amdgcn_s_waitcnt(0x0F70);  // no tile load may still be writing LDS when the pass ends
-    if (!workgroup_redo(bad_flag, sm.bad, wave, lane) || pass > 0) break;
+    if (!workgroup_redo<NW>(bad_flag, sm.bad, wave, lane) || pass > 0) break;
     sm.next_pass();
   }
 
@@ -954,7 +988,7 @@ __device__ __forceinline__ void bf16_fwd_dma(const FwdArgs& a, char* smem_generi
     lds_barrier();  // every wave is done with the last V tile: the buffers take the partial rows
     write_partial_staged<D>(a, w, o, 1.0f / l, lse_nat, h_half, smem + wave * (32 * D * 4), lane);
   } else if constexpr (!PARTIAL) {
-    static_assert(4 * 32 * D * 2 <= P::FLAGS, "four waves' output rows fit the tile buffers");
+    static_assert(NW * 32 * D * 2 <= 2 * NB * P::TILE_BYTES, "the waves' output rows fit the tile buffers");
     lds_barrier();  // every wave is done with the last V tile: the buffers take the output rows
     write_out_staged<D>(a, w, o, 1.0f / l, lse_nat, h_half, smem + wave * (32 * D * 2), lane);
   } else {
@@ -1576,16 +1610,18 @@ void attn_fwd_mixed_kernel(FwdArgs wide, FwdArgs narrow, int n_wide) {
   else bf16_fwd_dma<256, false, false>(narrow, smem);
 }
 
-template <class P, int D, bool PARTIAL, int WAVES_PER_EU, bool STREAM, bool MERGE = false>
-__global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads), amdgpu_waves_per_eu(WAVES_PER_EU, WAVES_PER_EU)))
+// NW waves per workgroup (8 only for the bf16 fused forward at D <= 128, see bf16_fwd_dma).
+template <class P, int D, bool PARTIAL, int WAVES_PER_EU, bool STREAM, bool MERGE = false, int NW = 4>
+__global__ __attribute__((amdgpu_flat_work_group_size(64 * NW, 64 * NW), amdgpu_waves_per_eu(WAVES_PER_EU, WAVES_PER_EU)))
 void attn_fwd_kernel(FwdArgs a) {
   static_assert(!MERGE || PARTIAL, "the merge tail follows a partial");
+  static_assert(NW == 4 || !P::kIsF32, "eight waves on the bf16 path only");
   if constexpr (P::kIsF32) {
     __shared__ __attribute__((aligned(16))) char smem[P::LDS_BYTES];
     attn_fwd_body<P, D, PARTIAL>(a, smem);
   } else {
-    __shared__ __attribute__((aligned(16))) char smem[P::LDS_BYTES];
-    bf16_fwd_dma<D, PARTIAL, STREAM>(a, smem);
+    __shared__ __attribute__((aligned(16))) char smem[dma_kernel_lds_bytes<D, NW>()];
+    bf16_fwd_dma<D, PARTIAL, STREAM, NW>(a, smem);
   }
   if constexpr (MERGE) splitkv_merge_tail<D, P::kIsF32>(a);
 }

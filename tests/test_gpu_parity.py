@@ -37,19 +37,22 @@ def _oracle(q, k, v, kv, scale):
     return ref_prefix_fwd(_np(q), _np(k), _np(v), kv.cpu().numpy(), scale)
 
 
-@pytest.fixture(params=[128, 256, "mixed"])
+@pytest.fixture(params=[128, "128x8", 256, "mixed"])
 def fwd_rows(request, monkeypatch):
-    """Force the bf16 forward path: 32 query rows per wave (128 per workgroup), 64 (256 per
-    workgroup), or, at D = 256, both in one grid (every full 256-row tile on the 64-row path,
-    the remaining rows on the 32-row one).  D = 64 has one kernel, D = 128 no mixed grid: those
-    cases are skipped, as is mixed where no 256-row tile is full or none is left over."""
+    """Force the bf16 forward path: 32 query rows per wave (128 per workgroup of four waves, or
+    256 per workgroup of eight at D <= 128), 64 (256 per workgroup), or, at D = 256, both in
+    one grid (every full 256-row tile on the 64-row path, the remaining rows on the 32-row
+    one).  D = 64 has no 64-row kernel, D = 128 no mixed grid, D = 256 no eight-wave form:
+    those cases are skipped, as is mixed where no 256-row tile is full or none is left over."""
     monkeypatch.setenv("ATTN_PREFIX_FWD_ROWS", str(request.param))
     return request.param
 
 
 def _skip_dup(D, rows, Tq=None):
-    if D == 64 and rows != 128:
-        pytest.skip("one bf16 forward kernel at this head dim")
+    if rows == "128x8" and D == 256:
+        pytest.skip("no eight-wave form at this head dim")
+    if D == 64 and rows not in (128, "128x8"):
+        pytest.skip("no 64-row kernel at this head dim")
     if D == 128 and rows == "mixed":
         pytest.skip("no mixed grid at this head dim")
     if rows == "mixed" and (Tq is None or Tq < 256 or Tq % 256 == 0):
@@ -509,6 +512,28 @@ def test_one_row_takes_second_pass(D, fwd_rows):
     out, lse = _run_fused(q, k, v, kv, scale)
     ro, rl = _oracle(q, k, v, kv, scale)
     assert_parity(out, lse, ro, rl, "bf16", f"one bad row D={D} rows={fwd_rows}")
+
+
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("Tq", [1, 200, 256, 257, 700, 1024])
+def test_eight_waves_same_bits(D, Tq, monkeypatch):
+    """The 32-row kernel with eight waves per workgroup (256 rows, four LDS buffers of K and
+    V, a barrier every other tile) runs the same per-row arithmetic as the four-wave form, so
+    its output and LSE bits must be identical, on both sides of every tile boundary and with
+    rows past T_q in the last workgroup."""
+    S = 700
+    lens = [0, 1, 63, 64, 65, 129, 300, S]
+    log(f"eight waves D={D} Tq={Tq} lens={lens}")
+    q, k, v, kv = make_inputs(len(lens), 2, Tq, S, D, lens, "bf16", 1.0, seed=2100 + Tq + D, device=DEV,
+                              pad=float("nan"))
+    scale = 1.0 / math.sqrt(D)
+    monkeypatch.setenv("ATTN_PREFIX_FWD_ROWS", "128")
+    o4, l4 = _run_fused(q, k, v, kv, scale)
+    monkeypatch.setenv("ATTN_PREFIX_FWD_ROWS", "128x8")
+    o8, l8 = _run_fused(q, k, v, kv, scale)
+    assert torch.equal(o4, o8) and torch.equal(l4, l8), "eight waves differ from four"
+    ro, rl = _oracle(q, k, v, kv, scale)
+    assert_parity(o8, l8, ro, rl, "bf16", f"eight waves D={D} Tq={Tq}")
 
 
 @pytest.mark.parametrize("Tq", [257, 300, 511, 700])

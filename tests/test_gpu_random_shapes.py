@@ -2,9 +2,9 @@
 
 Each case draws B, H, T_q, S, the per-element lengths (0 and S included at
 random), the head dim, the dtype and a scale of either sign, and runs the
-fused forward with each bf16 path forced (32 or 64 query rows per wave at
-D = 128 and 256, and both in one grid at D = 256), plus split-KV partials and
-their merge.
+fused forward with each bf16 path forced (32 query rows per wave with four or
+eight waves per workgroup at D <= 128, 64 rows per wave at D = 128 and 256, and
+both in one grid at D = 256), plus split-KV partials and their merge.
 """
 
 import math
@@ -49,7 +49,9 @@ def test_random_shape(i, monkeypatch):
     if dtype == "bf16" and D == 256:
         paths = ["128", "256", "mixed"]
     elif dtype == "bf16" and D == 128:
-        paths = ["128", "256"]
+        paths = ["128", "128x8", "256"]
+    elif dtype == "bf16":
+        paths = ["128", "128x8"]
     for rows in paths:
         monkeypatch.setenv("ATTN_PREFIX_FWD_ROWS", rows)
         out, lse = _lib.attn_prefix_fwd(q, k, v, kv, scale)
