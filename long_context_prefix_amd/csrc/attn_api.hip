@@ -76,7 +76,8 @@ attn_status_t launch_fwd(const FwdArgs& a, int64_t grid, hipStream_t stream, con
   const bool stream_kv = !P::kIsF32 && a.n_qtiles == 1;
   if (verbose())
     fprintf(stderr, "[attn_prefix] %s D=%d %s grid=%lld block=%d lds=%d waves_per_eu=%d%s\n", tag, D,
-            P::kIsF32 ? "f32" : "bf16", (long long)grid, kThreads, P::LDS_BYTES, W, stream_kv ? " streaming" : "");
+            P::kIsF32 ? "f32" : "bf16", (long long)grid, kThreads, P::kIsF32 ? P::LDS_BYTES : dma_kernel_lds_bytes<D, 4>(),
+            W, stream_kv ? " streaming" : "");
   (void)hipGetLastError();  // clear an error left by unrelated earlier calls
   if constexpr (!P::kIsF32) {
     if (stream_kv) {
@@ -232,7 +233,7 @@ attn_status_t launch_fwd_mixed(const FwdArgs& base, int B, int H, int W, hipStre
   const int64_t grid = n_wide + (int64_t)narrow.n_qtiles * B * H;
   if (verbose())
     fprintf(stderr, "[attn_prefix] prefix_fwd D=256 bf16 mixed grid=%lld (64-row %lld, 32-row %lld) lds=%d\n",
-            (long long)grid, (long long)n_wide, (long long)(grid - n_wide), Bf16Dma<256>::LDS_BYTES);
+            (long long)grid, (long long)n_wide, (long long)(grid - n_wide), dma_kernel_lds_bytes<256, 4>());
   (void)hipGetLastError();
   hipLaunchKernelGGL(attn_fwd_mixed_kernel, dim3((unsigned)grid), dim3(kThreads), 0, stream, wide, narrow,
                      (int)n_wide);

@@ -166,8 +166,7 @@ struct Bf16Dma {
   static constexpr int NBLK = kBN / RPB;   // blocks per tile (32, 16, 8)
   static constexpr int BLK = 1040;         // padded block stride
   static constexpr int TILE_BYTES = NBLK * BLK;
-  static constexpr int FLAGS = 4 * TILE_BYTES;      // K and V, two buffers each, then
-  static constexpr int LDS_BYTES = FLAGS + 4 * 4;   // one second-pass flag per wave
+  static constexpr int LDS_BYTES = 4 * TILE_BYTES;  // K and V (or Q and dO), two buffers each
   static constexpr int NQ = D / 16;
   static constexpr int LPR = ROWB / 16;    // DMA lanes per row
   static constexpr bool kIsF32 = false;
@@ -984,7 +983,7 @@ __device__ __forceinline__ void bf16_fwd_dma(const FwdArgs& a, char* smem_generi
   const float l = pair_sum(sm.l[0]);
   const float lse_nat = (sm.m[0] + __builtin_amdgcn_logf(l)) * kLn2;
   if constexpr (PARTIAL && STREAM) {
-    static_assert(4 * 32 * D * 4 <= P::FLAGS, "four waves' partial rows fit the tile buffers");
+    static_assert(NW * 32 * D * 4 <= 2 * NB * P::TILE_BYTES, "the waves' partial rows fit the tile buffers");
     lds_barrier();  // every wave is done with the last V tile: the buffers take the partial rows
     write_partial_staged<D>(a, w, o, 1.0f / l, lse_nat, h_half, smem + wave * (32 * D * 4), lane);
   } else if constexpr (!PARTIAL) {
@@ -1603,8 +1602,8 @@ void attn_fwd_wide_kernel(FwdArgs a) {
 // evenly than either kernel alone (e.g. 2 + 1 rounds instead of 2.5 or 5).
 __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads), amdgpu_waves_per_eu(1, 1)))
 void attn_fwd_mixed_kernel(FwdArgs wide, FwdArgs narrow, int n_wide) {
-  constexpr int kBytes = WideLayout<256>::LDS_BYTES > Bf16Dma<256>::LDS_BYTES ? WideLayout<256>::LDS_BYTES
-                                                                                : Bf16Dma<256>::LDS_BYTES;
+  constexpr int kBytes = WideLayout<256>::LDS_BYTES > dma_kernel_lds_bytes<256, 4>() ? WideLayout<256>::LDS_BYTES
+                                                                                      : dma_kernel_lds_bytes<256, 4>();
   __shared__ __attribute__((aligned(16))) char smem[kBytes];  // one allocation serves both paths
   if ((int)blockIdx.x < n_wide) bf16_fwd_wide<256, false, false>(wide, smem);
   else bf16_fwd_dma<256, false, false>(narrow, smem);
