@@ -1309,7 +1309,7 @@ __device__ __forceinline__ void bf16_fwd_wide(const FwdArgs& a, char* smem_gener
         f32x16& sg = g == 0 ? s0 : s1n;
         // the slot's share of the softmax goes before its MFMA, so that the VALU work fills the
         // time the operand read has to land before the MFMA waits for it (0.5-1% faster on
-        // most boxes measured)
+        // most of the GPUs measured)
         exp_slot(s1c, 1, i / SPE, p1, xe, pe, acc, SPE == 1 ? 2 : i % SPE);
         if (kk == 0) mfma_vgpr_first(sg, kf[kk % R], qf[g].v[0]);
         else mfma_vgpr_acc(sg, kf[kk % R], qf[g].v[kk]);
