@@ -51,8 +51,11 @@
  * of 256 threads at most 2^24 - 1 for the forward and split calls (the same
  * bound on ceil(B*H*Tq*D / 1024) for the merge, and on ceil(B*H*Tq*D / 2048),
  * B * H * ceil(Tq / 128) and B * H * ceil(S / 128) for the backward; B at most
- * 2^23 - 1 rows for the mask call).  Larger calls return ATTN_ERR_SHAPE before
- * any launch; size checks come before pointer checks.  Zero B, H or Tq is a no-op
+ * 2^23 - 1 rows for the mask call; B * H * ceil(Tq / 256) workgroups of 512
+ * threads at most 2^23 - 1 where the forward takes eight wavefronts per
+ * workgroup).  Larger calls return ATTN_ERR_SHAPE before any launch; size
+ * checks come before pointer checks (the eight-wave bound after them, since
+ * the kernel is chosen only then).  Zero B, H or Tq is a no-op
  * returning ATTN_OK (then the tensor pointers may be NULL); S = 0 is legal
  * (every n_b is 0) and then k and v may be NULL.
  */

@@ -133,6 +133,7 @@ template <int D>
 attn_status_t launch_fwd_8waves(FwdArgs a, int B, int H, hipStream_t stream) {
   a.n_qtiles = (a.Tq + kBM8 - 1) / kBM8;
   const int64_t grid = (int64_t)a.n_qtiles * B * H;
+  if (!grid_fits(grid, 8 * 64)) return ATTN_ERR_SHAPE;  // (check_fwd counted 256-thread workgroups)
   if (verbose())
     fprintf(stderr, "[attn_prefix] prefix_fwd D=%d bf16 8 waves grid=%lld block=%d lds=%d\n", D, (long long)grid,
             8 * 64, dma_kernel_lds_bytes<D, 8>());

@@ -247,6 +247,16 @@ def test_launch_limits_forward_and_split(L):
     assert split(L, po=None, B=MAX_WG // 3 + 1, S=192) == SHAPE
 
 
+def test_launch_limit_eight_wave_forward(L, monkeypatch):
+    """The eight-wave forward launches 512-thread workgroups, half as many as the size check
+    of the four-wave grid counted: its own grid is checked too (here B * H = 2^23 workgroups of
+    512 threads, 2^32 work-items, which the four-wave check lets through).  Only the failing
+    side is probed: a grid that fit would be launched."""
+    monkeypatch.setenv("ATTN_PREFIX_FWD_ROWS", "128x8")
+    assert fwd(L, B=2**23, D=128) == SHAPE
+    assert fwd(L, B=2**22, H=2, D=64) == SHAPE
+
+
 def test_launch_limits_single_launch_split(L):
     def call(**kw):
         a = dict(B=1, H=1, Tq=1, S=64)
