@@ -21,7 +21,7 @@ from tests.parity import assert_parity, log, to64
 pytestmark = pytest.mark.gpu
 
 DEV = "cuda"
-N_CASES = 48
+N_CASES = 96
 
 
 def _case(i):
