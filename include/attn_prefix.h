@@ -101,6 +101,10 @@ int attn_version(void);
  * wavefronts per workgroup, which give the same bits.  The environment variable
  * ATTN_PREFIX_FWD_ROWS=128, 128x8, 256 or mixed forces a choice (testing; 128x8
  * applies at D = 64 and 128, 256 at D = 128 and 256, mixed only at D = 256).
+ * Cost: the bf16 kernels read the valid keys once; a workgroup in which some row's
+ * scaled scores climb more than 20 log2 units (about 14 in natural-log units)
+ * above that row's maximum over its first key tile reads them a second time
+ * (same result; the split-KV partials do the same per chunk).
  */
 attn_status_t attn_prefix_fwd(const void* q, const void* k, const void* v, const int32_t* kv_len,
                               int B, int H, int Tq, int S, int D, float scale, attn_dtype_t dtype,
