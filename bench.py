@@ -142,6 +142,64 @@ def fetch_scaling(torch, _lib) -> int:
     return 0
 
 
+def wave_forms(torch, _lib, rounds: int, copy_calibration: bool) -> int:
+    """The ragged 32k forward (B=8, H=8, D=128) in the 32-row kernel's two forms, four
+    waves per workgroup (128 rows, two workgroups per CU) and eight (256 rows, one per
+    CU), launched alternately in one process so that both see the same clock.  Prints
+    each form's launch times from HIP events and checks that the two outputs are the
+    same bits.  Under a counter run the two forms are told apart by the wave count in
+    the kernel's name."""
+    from long_context_prefix_amd.workloads import WORKLOADS, make_workload
+
+    wb = WORKLOADS["ragged_32k"]
+    q, k, v, kv = make_workload(wb, device="cuda")
+    flop = 4.0 * wb.D * float(wb.H) * wb.Tq * float(wb.lens().sum())
+    forms = ("128", "128x8")
+    outs = {f: (torch.empty_like(q), torch.empty((wb.B, wb.H, wb.Tq), dtype=torch.float32, device="cuda"))
+            for f in forms}
+    prev = os.environ.get("ATTN_PREFIX_FWD_ROWS")
+
+    def launch(form):
+        os.environ["ATTN_PREFIX_FWD_ROWS"] = form
+        _lib.attn_prefix_fwd(q, k, v, kv, wb.scale, out=outs[form][0], lse=outs[form][1])
+
+    times = {f: [] for f in forms}
+    try:
+        for f in forms:
+            launch(f)
+        torch.cuda.synchronize()
+        for r in range(rounds):
+            for f in (forms if r % 2 == 0 else forms[::-1]):
+                s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                s.record()
+                launch(f)
+                e.record()
+                times[f].append((s, e))
+            log(f"wave forms: round {r + 1}/{rounds} done")
+        torch.cuda.synchronize()
+    finally:
+        if prev is None:
+            os.environ.pop("ATTN_PREFIX_FWD_ROWS", None)
+        else:
+            os.environ["ATTN_PREFIX_FWD_ROWS"] = prev
+    same = all(torch.equal(outs[forms[0]][i], outs[forms[1]][i]) for i in range(2))
+    if copy_calibration:
+        src = torch.empty(1 << 28, dtype=torch.float32, device="cuda").fill_(1.0)
+        torch.empty_like(src).copy_(src)
+        torch.cuda.synchronize()
+        log("copy calibration: 1 GiB read + 1 GiB written")
+    res = {}
+    for f in forms:
+        ms = sorted(s.elapsed_time(e) for s, e in times[f])
+        med = ms[len(ms) // 2]
+        res[f] = {"waves_per_workgroup": 8 if f.endswith("x8") else 4, "ms_median": round(med, 4),
+                  "ms_min": round(ms[0], 4), "tflops_median": round(flop / (med * 1e-3) / 1e12, 2)}
+    print(json.dumps({"wave_forms": res, "workload": wb.name, "B": wb.B, "H": wb.H, "head_dim": wb.D,
+                      "T_q": wb.Tq, "S": wb.S, "kv_len": [int(x) for x in wb.lens()], "launches_each": rounds,
+                      "same_bits": same}), flush=True)
+    return 0 if same else 1
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -157,6 +215,9 @@ def main() -> int:
     ap.add_argument("--fetch-scaling", action="store_true",
                     help="only run the fused kernel on one query tile per head over S=131072 slots with "
                          "n = S, S/2, S/4 (for HBM fetch counters: bytes read must follow n, not S)")
+    ap.add_argument("--wave-forms", type=int, default=0, metavar="R",
+                    help="only run the ragged 32k forward R times in each of the 32-row kernel's "
+                         "four- and eight-wave forms, alternately, and compare their times and bits")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -175,6 +236,8 @@ def main() -> int:
     src_hash = kernel_source_hash()
     if args.fetch_scaling:
         return fetch_scaling(torch, _lib)
+    if args.wave_forms:
+        return wave_forms(torch, _lib, args.wave_forms, args.copy_calibration)
 
     # ------------------------------------------------------------- fused path
     w = WORKLOADS["icl_121k"]
