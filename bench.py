@@ -119,6 +119,117 @@ def time_launches(fn, steps: int, torch):
     return wall, [s.elapsed_time(e) for s, e in evs]
 
 
+class GpuMeter:
+    """Power, clock and power-limit residency of the GPU that torch calls device 0,
+    from the amdsmi library.  The firmware refreshes its energy and residency counters
+    about once a second, so `measure` runs a launch back to back for a few seconds of its
+    own (outside any timed region) while a thread records each refresh, and reports
+    only whole refresh intervals inside that block.  Every figure is None where the
+    library, the device match or a counter is unavailable; the meter never fails the run."""
+
+    def __init__(self, torch):
+        self.torch = torch
+        self.smi = self.h = None
+        self.power_cap_w = None
+        try:
+            import amdsmi
+
+            amdsmi.amdsmi_init()
+            p = torch.cuda.get_device_properties(0)
+            want = f"{p.pci_domain_id:04x}:{p.pci_bus_id:02x}:{p.pci_device_id:02x}"
+            for h in amdsmi.amdsmi_get_processor_handles():
+                if amdsmi.amdsmi_get_gpu_device_bdf(h).lower().startswith(want):
+                    self.smi, self.h = amdsmi, h
+            if self.h is None:
+                log(f"energy: no amdsmi device at {want}")
+                return
+            cap = amdsmi.amdsmi_get_power_cap_info(self.h).get("power_cap")
+            # the library reports the cap in microwatts
+            self.power_cap_w = cap / 1e6 if isinstance(cap, (int, float)) and cap > 0 else None
+        except Exception as e:  # pragma: no cover - depends on the machine
+            log(f"energy: amdsmi unavailable ({type(e).__name__}: {e})")
+            self.smi = self.h = None
+
+    def _sample(self):
+        e = self.smi.amdsmi_get_energy_count(self.h)
+        r = {"t": time.perf_counter(), "ts": e["timestamp"],
+             "E": e["energy_accumulator"] * e["counter_resolution"] * 1e-6}  # resolution in uJ
+        try:
+            m = self.smi.amdsmi_get_gpu_metrics_info(self.h)
+            for k in ("accumulation_counter", "ppt_residency_acc"):
+                if isinstance(m.get(k), int):
+                    r[k] = m[k]
+            clks = [c for c in (m.get("current_gfxclks") or []) if isinstance(c, int)]
+            if clks:
+                r["clk"] = sum(clks) / len(clks)
+        except Exception:  # pragma: no cover
+            pass
+        return r
+
+    def measure(self, fn, seconds: float = 3.5, sync_every: int = 8):
+        """Run fn() (one launch each) back to back for `seconds`; returns power (W), mean
+        GFX clock over the XCDs (MHz), the share of the firmware's 1 ms ticks spent held
+        at the package power limit, and energy per launch (J)."""
+        if self.h is None:
+            return None
+        import threading
+
+        torch = self.torch
+        samples, stop = [], threading.Event()
+
+        def poll():
+            last = None
+            while not stop.is_set():
+                try:
+                    r = self._sample()
+                except Exception:  # pragma: no cover
+                    return
+                if last is None or r["ts"] != last:
+                    samples.append(r)
+                    last = r["ts"]
+                time.sleep(0.002)
+
+        th = threading.Thread(target=poll, daemon=True)
+        torch.cuda.synchronize()
+        th.start()
+        t0 = time.perf_counter()
+        n = 0
+        while time.perf_counter() - t0 < seconds:
+            for _ in range(sync_every):
+                fn()
+            n += sync_every
+            torch.cuda.synchronize()
+        t1 = time.perf_counter()
+        stop.set()
+        th.join(timeout=5)
+        return power_summary(samples, t0, t1, n, self.power_cap_w)
+
+
+def power_summary(samples, t0: float, t1: float, launches: int, power_cap_w=None):
+    """Power figures of a block [t0, t1] of `launches` back-to-back launches from the
+    firmware refreshes a polling thread recorded (host time t of first sight, firmware
+    timestamp ts in ns, energy E in J, 1 ms tick counter, power-limit ticks, clock).
+    Only refreshes first seen inside the block count, so each pair of them bounds a
+    whole firmware interval of the block's own work."""
+    inside = [r for r in samples if t0 + 0.01 < r["t"] <= t1]
+    out = {"power_cap_w": power_cap_w, "seconds": round(t1 - t0, 3), "launches": launches,
+           "refresh_intervals": max(0, len(inside) - 1)}
+    if len(inside) < 2 or inside[-1]["ts"] <= inside[0]["ts"]:
+        return out
+    a, b = inside[0], inside[-1]
+    p = (b["E"] - a["E"]) / ((b["ts"] - a["ts"]) * 1e-9)
+    out["mean_power_w"] = round(p, 1)
+    out["joules_per_launch"] = round(p * (t1 - t0) / launches, 4)
+    if "accumulation_counter" in a and "accumulation_counter" in b and "ppt_residency_acc" in a and "ppt_residency_acc" in b:
+        ticks = b["accumulation_counter"] - a["accumulation_counter"]
+        if ticks > 0:
+            out["power_limited_share"] = round((b["ppt_residency_acc"] - a["ppt_residency_acc"]) / ticks, 3)
+    clks = [r["clk"] for r in inside[1:] if "clk" in r]
+    if clks:
+        out["gfxclk_mhz_mean"] = round(sum(clks) / len(clks), 1)
+    return out
+
+
 def fetch_scaling(torch, _lib) -> int:
     """Fused launches at B=1, H=8, D=128, Tq=128 (one query tile per head, so each valid
     key row is fetched once) over S=131072 slots whose padded rows hold +-1e4, with
@@ -142,7 +253,7 @@ def fetch_scaling(torch, _lib) -> int:
     return 0
 
 
-def wave_forms(torch, _lib, rounds: int, copy_calibration: bool) -> int:
+def wave_forms(torch, _lib, rounds: int, copy_calibration: bool, meter=None) -> int:
     """The ragged 32k forward (B=8, H=8, D=128) in the 32-row kernel's two forms, four
     waves per workgroup (128 rows, two workgroups per CU) and eight (256 rows, one per
     CU), launched alternately in one process so that both see the same clock.  Prints
@@ -177,6 +288,12 @@ def wave_forms(torch, _lib, rounds: int, copy_calibration: bool) -> int:
                 times[f].append((s, e))
             log(f"wave forms: round {r + 1}/{rounds} done")
         torch.cuda.synchronize()
+        # power and clock: one block of a few seconds per form, in A B B A order
+        blocks = {f: [] for f in forms}
+        if meter is not None and meter.h is not None:
+            for f in forms + forms[::-1]:
+                blocks[f].append(meter.measure(lambda: launch(f)))
+                log(f"wave forms: power block of {f} done")
     finally:
         if prev is None:
             os.environ.pop("ATTN_PREFIX_FWD_ROWS", None)
@@ -194,6 +311,8 @@ def wave_forms(torch, _lib, rounds: int, copy_calibration: bool) -> int:
         med = ms[len(ms) // 2]
         res[f] = {"waves_per_workgroup": 8 if f.endswith("x8") else 4, "ms_median": round(med, 4),
                   "ms_min": round(ms[0], 4), "tflops_median": round(flop / (med * 1e-3) / 1e12, 2)}
+        if blocks[f]:
+            res[f]["power_blocks"] = blocks[f]
     print(json.dumps({"wave_forms": res, "workload": wb.name, "B": wb.B, "H": wb.H, "head_dim": wb.D,
                       "T_q": wb.Tq, "S": wb.S, "kv_len": [int(x) for x in wb.lens()], "launches_each": rounds,
                       "same_bits": same}), flush=True)
@@ -218,6 +337,9 @@ def main() -> int:
     ap.add_argument("--wave-forms", type=int, default=0, metavar="R",
                     help="only run the ragged 32k forward R times in each of the 32-row kernel's "
                          "four- and eight-wave forms, alternately, and compare their times and bits")
+    ap.add_argument("--energy", action="store_true",
+                    help="after each timed leg (and per --wave-forms form), run its launch for a few more "
+                         "seconds and report power, clock and power-limit residency from amdsmi")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -237,7 +359,8 @@ def main() -> int:
     if args.fetch_scaling:
         return fetch_scaling(torch, _lib)
     if args.wave_forms:
-        return wave_forms(torch, _lib, args.wave_forms, args.copy_calibration)
+        return wave_forms(torch, _lib, args.wave_forms, args.copy_calibration,
+                          GpuMeter(torch) if args.energy else None)
 
     # ------------------------------------------------------------- fused path
     w = WORKLOADS["icl_121k"]
@@ -254,6 +377,7 @@ def main() -> int:
     for _ in range(args.warmup):
         fused()
     torch.cuda.synchronize()
+    meter = GpuMeter(torch) if args.energy else None
     log(f"timing {args.steps} fused steps")
     wall, ms = time_launches(fused, args.steps, torch)
     ms_avg = sum(ms) / len(ms)
@@ -287,6 +411,12 @@ def main() -> int:
         "roofline": roofline,
         "kernel_source_sha256_16": src_hash,
     }
+    if meter:
+        en = meter.measure(fused, sync_every=2)
+        if en and "joules_per_launch" in en:
+            en["tflop_per_joule"] = round(flops / 1e12 / en["joules_per_launch"], 3)
+        result["power"] = en
+        log(f"power: {en}")
 
     invalid = []  # parity failures of timed outputs: the line then carries no value
 
@@ -376,6 +506,13 @@ def main() -> int:
         gbs = alg_bytes / ((t_part + t_comb) * 1e-3) / 1e9
         part_gbs = (alg_bytes - float(ws.B * ws.H * (ws.Tq * ws.D * esz + ws.Tq * 4)) + part_bytes) / (t_part * 1e-3) / 1e9
         log(f"split-KV: partial {t_part:.3f} ms, combine {t_comb:.3f} ms, {gbs:.0f} GB/s algorithmic")
+        en_s = None
+        if meter:
+            def step_s():
+                partial()
+                combine()
+            en_s = meter.measure(step_s)
+            log(f"split-KV power: {en_s}")
         result["splitkv"] = {
             "workload": ws.name, "B": ws.B, "H": ws.H, "head_dim": ws.D, "T_q": ws.Tq, "S": ws.S, "n": int(slens[0]),
             "chunk": ws.chunk, "chunks": C,
@@ -391,6 +528,8 @@ def main() -> int:
                 "bytes_counted": "Q + valid K/V + fp32 partial write",
             },
         }
+        if en_s is not None:
+            result["splitkv"]["power"] = en_s
         if not args.no_cpu_baseline:
             # the oracle on whole sequences of the timed output (the first and a seeded one):
             # parity of the split-KV leg, and its CPU baseline in the same unit
@@ -508,6 +647,10 @@ def main() -> int:
         t_b = sum(b.elapsed_time(c) for _, b, c in evs) / steps
         alg_b = 10.0 * wb.D * pairs  # dV, dP, dQ, dK and the recomputed S: five products of 2 D per pair
         log(f"backward: fwd {t_f:.3f} ms, bwd {t_b:.3f} ms, {alg_b / (t_b * 1e-3) / 1e12:.1f} TFLOP/s")
+        en_b = None
+        if meter:
+            en_b = meter.measure(bwd_b, sync_every=4)
+            log(f"backward power: {en_b}")
         result["backward"] = {
             "workload": wb.name, "B": wb.B, "H": wb.H, "head_dim": wb.D, "T_q": wb.Tq, "S": wb.S,
             "kv_len": [int(x) for x in blens],
@@ -519,6 +662,8 @@ def main() -> int:
             "executed_tflops": round(14.0 * wb.D * pairs / (t_b * 1e-3) / 1e12, 2),
             "kernels": "bwd_delta_kernel, bwd_dq_slot_kernel (S, dP, dQ), bwd_dkdv_pipe_kernel (S, dP, dV, dK)",
         }
+        if en_b is not None:
+            result["backward"]["power"] = en_b
         del q, k, v, out, lse, dout, dq, dk, dv, delta
         torch.cuda.empty_cache()
 

@@ -96,3 +96,33 @@ def test_bench_parity_gate():
     nan_out[0, 0] = np.nan
     assert bench.parity_failures(bench.parity_stats(np, nan_out, lse, ref, lse))  # NaN never passes
     assert bench.parity_failures(bench.parity_stats(np, ref, np.array([1.0, 0.0]), ref, lse))  # -inf pattern
+
+
+def test_bench_power_summary_uses_whole_refresh_intervals():
+    """The power figures come only from firmware refreshes first seen inside the block:
+    a block of 3.5 s at 1,300 W with refreshes every second, a refresh before the block
+    and one after it (both at other powers) must not move the result."""
+    sys.path.insert(0, ROOT)
+    import bench
+
+    t0, t1, watts = 10.0, 13.5, 1300.0
+    samples = [{"t": 9.7, "ts": int(9.69e9), "E": 0.0, "accumulation_counter": 0, "ppt_residency_acc": 0, "clk": 158.0}]
+    e, ticks, ppt = 50.0, 0, 0  # the refresh before the block saw an idle GPU
+    for i, t in enumerate((10.3, 11.3, 12.3, 13.3)):
+        if i:
+            e += watts * 1.0
+            ticks += 1000
+            ppt += 750
+        samples.append({"t": t, "ts": int((t - 0.001) * 1e9), "E": e, "accumulation_counter": ticks,
+                        "ppt_residency_acc": ppt, "clk": 1800.0})
+    samples.append({"t": 14.3, "ts": int(14.299e9), "E": e + 300.0, "accumulation_counter": ticks + 1000,
+                    "ppt_residency_acc": ppt, "clk": 158.0})
+    r = bench.power_summary(samples, t0, t1, 70, 1400.0)
+    assert r["refresh_intervals"] == 3
+    assert abs(r["mean_power_w"] - watts) < 0.5
+    assert abs(r["joules_per_launch"] - watts * 3.5 / 70) < 1e-3
+    assert r["power_limited_share"] == 0.75
+    assert r["gfxclk_mhz_mean"] == 1800.0
+    # fewer than two refreshes inside: no power figure rather than a wrong one
+    r = bench.power_summary(samples[:2] + samples[-1:], t0, t1, 70, 1400.0)
+    assert r["refresh_intervals"] == 0 and "mean_power_w" not in r
