@@ -35,8 +35,10 @@
  * current device); `stream` is a hipStream_t passed as void* (NULL = the null
  * stream).  Calls only enqueue work on `stream` and return; buffers must stay
  * alive until that work completes.  The caller owns every buffer: the library
- * allocates no memory, keeps no pointer after a call returns and holds no
- * mutable global state, so calls are re-entrant.
+ * allocates no memory, keeps no caller pointer after a call returns and holds no
+ * mutable global state, so calls are re-entrant.  The one exception is
+ * attn_prefix_bwd_noalloc, whose workspace is a device array of the library
+ * shared by every call on a GPU (see there).
  *
  * Errors.  Every call validates its arguments on the host BEFORE any HIP call
  * and returns a status code; no call ever falls back to another algorithm.
@@ -135,9 +137,11 @@ attn_status_t attn_splitkv_partial(const void* q, const void* k, const void* v, 
  *              a counters buffer must not run concurrently.
  *   out, lse : as for attn_lse_combine, out in `dtype` (lse may be NULL)
  * The merged result is bit-identical to attn_splitkv_partial followed by
- * attn_lse_combine.  On MI355X it is slower than those two calls (10.7 ms vs
- * 6.3 ms on 160 x 4 heads x 100,000 keys): each chunk's device-scope release
- * writes back its XCD's L2, which costs more than the second launch it saves.
+ * attn_lse_combine.  On MI355X it is slower than those two calls (7.8-8.1 ms
+ * against 5.6-6.0 ms on 160 x 4 heads x 100,000 keys in 4,096-key chunks): each
+ * merge is one workgroup reading partials that other XCDs' L2 caches just wrote
+ * back, while the other chunks' loads stream past, and those merges cost more
+ * than the second launch they save.
  * Errors as for attn_splitkv_partial, plus ATTN_ERR_NULLPTR
  * (counters or out NULL) and ATTN_ERR_ALIGN (counters/lse not 4-byte aligned,
  * out not 16-byte aligned). */
