@@ -134,3 +134,23 @@ def test_full_size_determinism_and_padding_invariance(name):
     out3, lse3 = _lib.attn_prefix_fwd(q, k, v, kv, w.scale)
     torch.cuda.synchronize()
     assert torch.equal(out, out3) and torch.equal(lse, lse3), "padded slots changed the result"
+
+
+@pytest.mark.timeout(900)
+def test_ragged_32k_wave_forms_same_bits(monkeypatch):
+    """At the ragged 32k shape the host takes the eight-wave form of the 32-row kernel; the
+    four-wave form, forced, must give the same output and LSE bits (the same per-row
+    arithmetic), and the default launch must be one of the two."""
+    w = WORKLOADS["ragged_32k"]
+    log(f"workload ragged_32k: four- against eight-wave form, kv_len={w.lens().tolist()}")
+    q, k, v, kv = make_workload(w, device=DEV)
+    res = {}
+    for form in ("128", "128x8", None):
+        if form is None:
+            monkeypatch.delenv("ATTN_PREFIX_FWD_ROWS", raising=False)
+        else:
+            monkeypatch.setenv("ATTN_PREFIX_FWD_ROWS", form)
+        res[form] = _lib.attn_prefix_fwd(q, k, v, kv, w.scale)
+    torch.cuda.synchronize()
+    for form in ("128x8", None):
+        assert torch.equal(res["128"][0], res[form][0]) and torch.equal(res["128"][1], res[form][1]), form
