@@ -79,6 +79,14 @@ def _check(fn: str, code: int) -> None:
         raise AttnError(fn, code, status_string(code))
 
 
+def _call(fn: str, dev: torch.device, *args) -> None:
+    """Call a library entry point with `dev` as the current HIP device (the library launches
+    on the current device, which must be the one that holds the tensors) and raise on error."""
+    with torch.cuda.device(dev):
+        code = getattr(load(), fn)(*args)
+    _check(fn, code)
+
+
 def _dtype_code(t: torch.Tensor) -> int:
     if t.dtype == torch.bfloat16:
         return ATTN_BF16
@@ -141,9 +149,8 @@ def attn_prefix_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, kv_len: t
         _require(lse, "lse", dev)
         if lse.shape != (B, H, Tq) or lse.dtype != torch.float32:
             raise ValueError("lse must be fp32 [B, H, Tq]")
-    code = load().attn_prefix_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(kv_len), B, H, Tq, S, D, scale,
-                                  _dtype_code(q), _ptr(out), _ptr(lse), _stream(dev))
-    _check("attn_prefix_fwd", code)
+    _call("attn_prefix_fwd", dev, _ptr(q), _ptr(k), _ptr(v), _ptr(kv_len), B, H, Tq, S, D, scale,
+          _dtype_code(q), _ptr(out), _ptr(lse), _stream(dev))
     return out, lse
 
 
@@ -165,9 +172,8 @@ def attn_splitkv_partial(q, k, v, kv_len, chunk: int, scale: Optional[float] = N
         raise ValueError("partial buffers have the wrong shape")
     if part_out.dtype != torch.float32 or part_lse.dtype != torch.float32:
         raise ValueError("partial buffers must be fp32")
-    code = load().attn_splitkv_partial(_ptr(q), _ptr(k), _ptr(v), _ptr(kv_len), B, H, Tq, S, D, scale,
-                                       _dtype_code(q), int(chunk), _ptr(part_out), _ptr(part_lse), _stream(dev))
-    _check("attn_splitkv_partial", code)
+    _call("attn_splitkv_partial", dev, _ptr(q), _ptr(k), _ptr(v), _ptr(kv_len), B, H, Tq, S, D, scale,
+          _dtype_code(q), int(chunk), _ptr(part_out), _ptr(part_lse), _stream(dev))
     return part_out, part_lse
 
 
@@ -188,9 +194,8 @@ def attn_lse_combine(part_out: torch.Tensor, part_lse: torch.Tensor, out_dtype=t
     _require(out, "out", dev)
     if lse is not None:
         _require(lse, "lse", dev)
-    code = load().attn_lse_combine(_ptr(part_out), _ptr(part_lse), B, H, C, Tq, D, _dtype_code(out), _ptr(out),
-                                   _ptr(lse), _stream(dev))
-    _check("attn_lse_combine", code)
+    _call("attn_lse_combine", dev, _ptr(part_out), _ptr(part_lse), B, H, C, Tq, D, _dtype_code(out), _ptr(out),
+          _ptr(lse), _stream(dev))
     return out, lse
 
 
@@ -225,9 +230,8 @@ def attn_prefix_mask_to_kv_len(mask: torch.Tensor, kv_len: Optional[torch.Tensor
         kv_len = torch.empty(B, dtype=torch.int32, device=mask.device)
     elif kv_len.dtype != torch.int32 or kv_len.shape != (B,) or kv_len.device != mask.device:
         raise ValueError("kv_len must be int32 [B] on the mask's device")
-    code = load().attn_prefix_mask_to_kv_len(_ptr(mask), B, S, int(row_stride), _ptr(kv_len),
-                                             _stream(mask.device))
-    _check("attn_prefix_mask_to_kv_len", code)
+    _call("attn_prefix_mask_to_kv_len", mask.device, _ptr(mask), B, S, int(row_stride), _ptr(kv_len),
+          _stream(mask.device))
     return kv_len
 
 
@@ -278,10 +282,9 @@ def attn_prefix_bwd(q, k, v, kv_len, out, dout, lse, scale: Optional[float] = No
     _require(delta, "delta", dev)
     if delta.shape != (B, H, Tq) or delta.dtype != torch.float32:
         raise ValueError("delta must be fp32 [B, H, Tq]")
-    code = load().attn_prefix_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(kv_len), _ptr(out), _ptr(dout), _ptr(lse),
-                                  B, H, Tq, S, D, scale, _dtype_code(q), _ptr(delta), _ptr(dq), _ptr(dk), _ptr(dv),
-                                  _stream(dev))
-    _check("attn_prefix_bwd", code)
+    _call("attn_prefix_bwd", dev, _ptr(q), _ptr(k), _ptr(v), _ptr(kv_len), _ptr(out), _ptr(dout), _ptr(lse),
+          B, H, Tq, S, D, scale, _dtype_code(q), _ptr(delta), _ptr(dq), _ptr(dk), _ptr(dv),
+          _stream(dev))
     return dq, dk, dv
 
 
@@ -299,10 +302,9 @@ def attn_prefix_bwd_noalloc(q, k, v, kv_len, out, dout, lse, dq, dk, dv, scale: 
     _require(lse, "lse", dev)
     if lse.shape != (B, H, Tq) or lse.dtype != torch.float32:
         raise ValueError("lse must be fp32 [B, H, Tq]")
-    code = load().attn_prefix_bwd_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(kv_len), _ptr(out), _ptr(dout), _ptr(lse),
-                                          B, H, Tq, S, D, scale, _dtype_code(q), _ptr(dq), _ptr(dk), _ptr(dv),
-                                          _stream(dev))
-    _check("attn_prefix_bwd_noalloc", code)
+    _call("attn_prefix_bwd_noalloc", dev, _ptr(q), _ptr(k), _ptr(v), _ptr(kv_len), _ptr(out), _ptr(dout), _ptr(lse),
+          B, H, Tq, S, D, scale, _dtype_code(q), _ptr(dq), _ptr(dk), _ptr(dv),
+          _stream(dev))
     return dq, dk, dv
 
 
@@ -366,8 +368,7 @@ def attn_splitkv_fwd(q, k, v, kv_len, chunk: int, scale: Optional[float] = None,
         _require(lse, "lse", dev)
         if lse.shape != (B, H, Tq) or lse.dtype != torch.float32:
             raise ValueError("lse must be fp32 [B, H, Tq]")
-    code = load().attn_splitkv_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(kv_len), B, H, Tq, S, D, scale, _dtype_code(q),
-                                   int(chunk), _ptr(part_out), _ptr(part_lse), _ptr(counters), _ptr(out), _ptr(lse),
-                                   _stream(dev))
-    _check("attn_splitkv_fwd", code)
+    _call("attn_splitkv_fwd", dev, _ptr(q), _ptr(k), _ptr(v), _ptr(kv_len), B, H, Tq, S, D, scale, _dtype_code(q),
+          int(chunk), _ptr(part_out), _ptr(part_lse), _ptr(counters), _ptr(out), _ptr(lse),
+          _stream(dev))
     return out, lse
