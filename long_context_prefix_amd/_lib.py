@@ -185,15 +185,23 @@ def attn_lse_combine(part_out: torch.Tensor, part_lse: torch.Tensor, out_dtype=t
         raise ValueError("part_out must be [B,H,C,Tq,D] and part_lse [B,H,C,Tq]")
     B, H, C, Tq, D = part_out.shape
     dev = part_out.device
+    if dev.type != "cuda":
+        raise ValueError("tensors must live on a GPU")
     _require(part_out, "part_out", dev)
     _require(part_lse, "part_lse", dev)
+    if part_out.dtype != torch.float32 or part_lse.dtype != torch.float32:
+        raise ValueError("partial buffers must be fp32")
     if out is None:
         out = torch.empty((B, H, Tq, D), dtype=out_dtype, device=dev)
     if lse is None and return_lse:
         lse = torch.empty((B, H, Tq), dtype=torch.float32, device=dev)
     _require(out, "out", dev)
+    if out.shape != (B, H, Tq, D):
+        raise ValueError("out must be [B, H, Tq, D]")
     if lse is not None:
         _require(lse, "lse", dev)
+        if lse.shape != (B, H, Tq) or lse.dtype != torch.float32:
+            raise ValueError("lse must be fp32 [B, H, Tq]")
     _call("attn_lse_combine", dev, _ptr(part_out), _ptr(part_lse), B, H, C, Tq, D, _dtype_code(out), _ptr(out),
           _ptr(lse), _stream(dev))
     return out, lse
