@@ -248,7 +248,7 @@ void bwd_dq_slot_kernel(BwdArgs a) {
       }
       __builtin_amdgcn_sched_barrier(0);
     }
-    xdl_result_guard();  // the softmax below reads the half-0 results
+    xdl_result_guard<1>();  // the softmax below reads the half-0 results
     if (nv < kBN) {
       rare_path();
       mask_half(s[0], 0, nv);
@@ -265,7 +265,7 @@ void bwd_dq_slot_kernel(BwdArgs a) {
         if (j * EB + u < 16) elem(0, j * EB + u);
       __builtin_amdgcn_sched_barrier(0);
     }
-    xdl_result_guard();  // the softmax below reads the half-1 results
+    xdl_result_guard<1>();  // the softmax below reads the half-1 results
     if (nv < kBN) {
       rare_path();
       mask_half(s[1], 1, nv);
@@ -482,7 +482,7 @@ void bwd_dkdv_slot_kernel(BwdArgs a) {
       __builtin_amdgcn_sched_barrier(0);
     }
     nd = neg_delta16(1);  // for the dP chain of phase B
-    xdl_result_guard();
+    xdl_result_guard<14>();
     // phase B: S, dP of queries 32..63; P, dS of queries 0..31
 #pragma unroll
     for (int j = 0; j < NH; ++j) {
@@ -495,7 +495,7 @@ void bwd_dkdv_slot_kernel(BwdArgs a) {
       __builtin_amdgcn_sched_barrier(0);
     }
     Lq[0] = stat4(4, 0);  // group 4 opens the second half
-    xdl_result_guard();
+    xdl_result_guard<12>();
     // phase C: dV, dK over queries 0..31; P, dS of queries 32..63
 #pragma unroll
     for (int j = 0; j < NC; ++j) {

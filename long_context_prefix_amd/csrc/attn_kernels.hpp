@@ -133,12 +133,40 @@ __device__ __forceinline__ void mfma_agpr_acc(f32x16& o, bf16x8 a, u32x4 b) {
   asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(o) : "v"(a), "v"(b));
 }
 
-// 24 wait states between the last of those MFMAs and any VALU read of their
-// results (about twice what a 32x32x16 MFMA needs); the scheduling fences keep
-// the compiler from moving work across.
+// W wait states of s_nop (s_nop N gives N + 1).  Every VALU read of an inline-MFMA result
+// must come at least 24 wait states after that MFMA on every path (about twice what a
+// 32x32x16 MFMA needs); the build's ISA check proves it on the assembly.  Each guard takes
+// the fewest nops that, added to the instructions the schedule already places in between,
+// reach that distance, since the nops cost issue cycles on every tile.
+template <int W>
+__device__ __forceinline__ void xdl_nops() {
+  static_assert(W >= 0 && W <= 32, "wait states");
+  if constexpr (W >= 8) {
+    asm volatile("s_nop 7" ::: "memory");
+    xdl_nops<W - 8>();
+  } else if constexpr (W == 7) {
+    asm volatile("s_nop 6" ::: "memory");
+  } else if constexpr (W == 6) {
+    asm volatile("s_nop 5" ::: "memory");
+  } else if constexpr (W == 5) {
+    asm volatile("s_nop 4" ::: "memory");
+  } else if constexpr (W == 4) {
+    asm volatile("s_nop 3" ::: "memory");
+  } else if constexpr (W == 3) {
+    asm volatile("s_nop 2" ::: "memory");
+  } else if constexpr (W == 2) {
+    asm volatile("s_nop 1" ::: "memory");
+  } else if constexpr (W == 1) {
+    asm volatile("s_nop 0" ::: "memory");
+  }
+}
+
+// W wait states before the VALU reads of the results of the MFMAs above; the scheduling
+// fences keep the compiler from moving work across.
+template <int W = 24>
 __device__ __forceinline__ void xdl_result_guard() {
   __builtin_amdgcn_sched_barrier(0);
-  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
+  xdl_nops<W>();
   __builtin_amdgcn_sched_barrier(0);
 }
 
@@ -923,10 +951,9 @@ __device__ __forceinline__ void bf16_fwd_dma(const FwdArgs& a, char* smem_generi
         sm.bad = true;
         sm.mtop[0] = fmaxf(sm.mtop[0], row_max64(sc, c));
       }
-      // the scores were written by MFMAs the compiler does not see as such: keep the
-      // VALU reads of S_{j+1} below clear of the last of them (16 wait states here,
-      // on top of the two MFMA issues in between)
-      asm volatile("s_nop 7\n\ts_nop 7" ::: "memory");
+      // the scores were written by MFMAs the compiler does not see as such; the work
+      // scheduled since the last of them already keeps the VALU reads of S_{j+1} below
+      // the 24 wait states clear of it (the build's ISA check proves it), so no nops
       __builtin_amdgcn_sched_barrier(0);
       if (nv_of(j + 1) < kBN) {
         rare_path();
@@ -971,7 +998,7 @@ __device__ __forceinline__ void bf16_fwd_dma(const FwdArgs& a, char* smem_generi
         if (kk == 0) mfma_vgpr_first(s_cur[kb], kf, qf.v[0]);
         else mfma_vgpr_acc(s_cur[kb], kf, qf.v[kk]);
       }
-    asm volatile("s_nop 7\n\ts_nop 7" ::: "memory");  // XDL result -> VALU read (row max below)
+    xdl_nops<24>();  // XDL result -> VALU read (row max below)
     __syncthreads();  // every wave is done with K_0 before its buffer is refilled
     if (nv_of(0) < kBN) mask_scores(s_cur, nv_of(0));
     if (pass == 0) sm.m[0] = row_max64(s_cur, c);  // the first tile's max is the first pass's reference
@@ -1102,10 +1129,13 @@ __device__ __forceinline__ Work next_group(const FwdArgs& a, Work w) {
 __device__ __forceinline__ void o_result_guard(f32x16& o) {
   asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+a"(o));
 }
-// The same for two score blocks before their first VALU read.
+// The same for two score blocks before their first VALU read (W wait states of nops,
+// then an empty asm that takes the blocks as operands).
+template <int W>
 __device__ __forceinline__ void s_result_guard(f32x16& s0, f32x16& s1) {
   __builtin_amdgcn_sched_barrier(0);
-  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+v"(s0), "+v"(s1));
+  xdl_nops<W>();
+  asm volatile("" : "+v"(s0), "+v"(s1));
   __builtin_amdgcn_sched_barrier(0);
 }
 
@@ -1333,7 +1363,7 @@ __device__ __forceinline__ void bf16_fwd_wide(const FwdArgs& a, char* smem_gener
     }
     // the scores were written by MFMAs the compiler does not see as such: keep the VALU
     // reads of S_{j+1} below clear of the last of them
-    s_result_guard(s0, s1n);
+    s_result_guard<13>(s0, s1n);
     if (nv < kBNW) {
       rare_path();
       mask_scores(s0, s1n, nv);
@@ -1389,7 +1419,7 @@ __device__ __forceinline__ void bf16_fwd_wide(const FwdArgs& a, char* smem_gener
         mfma_vgpr_acc(s1a, kf, qf[1].v[kk]);
       }
     }
-    s_result_guard(s0, s1a);  // XDL result -> VALU read (row max below)
+    s_result_guard<24>(s0, s1a);  // XDL result -> VALU read (row max below)
     __syncthreads();          // every wave is done with K_0 before its buffer is refilled
     if (nv_of(0) < kBNW) mask_scores(s0, s1a, nv_of(0));
     // the first tile's max is the reference of a first pass; group 0's exponentials are

@@ -9,13 +9,17 @@ so it cannot insert the wait states the hardware needs between an XDL
 instruction that writes a register and a later instruction that reads it (or
 writes it again).  The kernels leave those wait states by construction; this
 check proves it on the actual assembly after every build: for every inline
-``v_mfma`` it walks the following instructions, counting one wait state per
-instruction and N + 1 per ``s_nop N``, and reports any VALU instruction
-(``v_accvgpr_read`` included), LDS or memory store that reads one of the
-result registers, and any VALU instruction or load that overwrites one, before
-``WAIT_STATES`` have passed, and any VALU write of one of its operands fewer
-than ``OPERAND_WAIT_STATES`` before it.  Using the result as the accumulator of
-the next MFMA of the same chain is the one allowed access.
+``v_mfma`` it walks every path of instructions that can follow it, counting one
+wait state per instruction and N + 1 per ``s_nop N`` (a conditional branch
+continues both into the next instruction and at its target, a jump at its
+target, so a block that the common path branches over is not counted as
+distance), and reports any VALU instruction (``v_accvgpr_read`` included), LDS
+or memory store that reads one of the result registers, and any VALU
+instruction or load that overwrites one, before ``WAIT_STATES`` have passed on
+some path; and, walking back along every path that can lead to the MFMA, any
+VALU write of one of its operands fewer than ``OPERAND_WAIT_STATES`` before it.
+Using the result as the accumulator of the next MFMA of the same chain is the
+one allowed access.
 """
 
 from __future__ import annotations
@@ -65,8 +69,111 @@ def _accesses(line: str):
     return reads, writes
 
 
+_LABEL = re.compile(r"^(\.L\w+):")
+_STOP = ("s_endpgm", "s_setpc_b64", "s_trap")
+
+
+def _is_code(t: str) -> bool:
+    return bool(t) and not t.startswith(";") and not t.startswith(".") and not t.endswith(":")
+
+
+def _branch(t: str):
+    """(target label, conditional?) of a branch instruction, else None."""
+    op = t.split()[0]
+    if op == "s_branch":
+        return t.split()[-1], False
+    if op.startswith("s_cbranch_"):
+        return t.split()[-1], True
+    return None
+
+
+def _cost(t: str) -> int:
+    return int(t.split()[1], 0) + 1 if t.split()[0] == "s_nop" else 1
+
+
 def inline_mfma_hazards(asm: str, wait_states: int = WAIT_STATES) -> List[str]:
     lines = [l.strip() for l in asm.split("\n")]
+    labels = {}
+    for k, t in enumerate(lines):
+        m = _LABEL.match(t)
+        if m:
+            labels[m.group(1)] = k
+    # predecessors of each label line: the branches that target it (the line before it
+    # falls through unless it is a jump or an end)
+    branches_to = {}
+    for k, t in enumerate(lines):
+        if _is_code(t):
+            b = _branch(t)
+            if b and b[0] in labels:
+                branches_to.setdefault(labels[b[0]], []).append(k)
+
+    def walk_forward(start: int, dst: set, mfma: str, kernel: str, found: list) -> None:
+        best = {}  # line -> fewest wait states it was reached with
+        work = [(start, 0)]
+        reported = set()
+        while work:
+            j, ws = work.pop()
+            while j < len(lines) and ws < wait_states:
+                if best.get(j, wait_states + 1) <= ws:
+                    break
+                best[j] = ws
+                u = lines[j]
+                if _KERNEL.match(u):
+                    break
+                if not _is_code(u):
+                    j += 1
+                    continue
+                op = u.split()[0]
+                if op in _STOP:
+                    break
+                b = _branch(u)
+                ws_here = ws + _cost(u)
+                if op != "s_nop" and not op.startswith("v_mfma") and b is None:
+                    reads, writes = _accesses(u)
+                    key = (j, "r" if reads & dst else "w" if writes & dst else "")
+                    if key[1] and key not in reported:
+                        reported.add(key)
+                        what = "reads the result of" if key[1] == "r" else "overwrites the result of"
+                        found.append(f"{kernel}: '{u}' {what} '{mfma}' after {ws_here} wait states")
+                ws = ws_here
+                if b is not None:
+                    target, conditional = b
+                    if target in labels:
+                        work.append((labels[target], ws))
+                    if not conditional:
+                        break
+                j += 1
+
+    def walk_back(start: int, srcs: set, mfma: str, kernel: str, found: list) -> None:
+        best = {}
+        work = [(start - 1, 0)]
+        reported = set()
+        while work:
+            j, ws = work.pop()
+            while j >= 0 and ws < OPERAND_WAIT_STATES:
+                if best.get(j, OPERAND_WAIT_STATES + 1) <= ws:
+                    break
+                best[j] = ws
+                u = lines[j]
+                if _KERNEL.match(u):
+                    break
+                if j in branches_to:  # a label line: other paths arrive here too
+                    for k in branches_to[j]:
+                        work.append((k, ws))
+                if not _is_code(u):
+                    j -= 1
+                    continue
+                b = _branch(u)
+                if b is not None and not b[1] and j != start - 1:
+                    break  # a jump elsewhere: this line is not on a path into the MFMA
+                op = u.split()[0]
+                if op.startswith("v_") and not op.startswith("v_mfma") and _accesses(u)[1] & srcs:
+                    if j not in reported:
+                        reported.add(j)
+                        found.append(f"{kernel}: '{mfma}' reads an operand written by '{u}' after {ws} wait states")
+                ws += _cost(u)
+                j -= 1
+
     found = []
     kernel = "?"
     in_asm = False
@@ -86,43 +193,11 @@ def inline_mfma_hazards(asm: str, wait_states: int = WAIT_STATES) -> List[str]:
         dst = _regs(parts[1].split(",")[0]) if len(parts) > 1 else set()
         if not dst:
             continue
-        # the operands must not have been written by a VALU instruction just before
         srcs = set()
         for o in _operands(t)[1:]:
             srcs |= _regs(o)
-        ws = 0
-        j = i - 1
-        while j >= 0 and ws < OPERAND_WAIT_STATES:
-            u = lines[j]
-            j -= 1
-            if not u or u.startswith(";") or u.startswith(".") or u.endswith(":"):
-                continue
-            op = u.split()[0]
-            if op == "s_nop":
-                ws += int(u.split()[1], 0) + 1
-                continue
-            if op.startswith("v_") and not op.startswith("v_mfma") and _accesses(u)[1] & srcs:
-                found.append(f"{kernel}: '{t}' reads an operand written by '{u}' after {ws} wait states")
-            ws += 1
-        ws = 0
-        j = i + 1
-        while j < len(lines) and ws < wait_states:
-            u = lines[j]
-            j += 1
-            if not u or u.startswith(";") or u.startswith(".") or u.endswith(":"):
-                continue
-            op = u.split()[0]
-            if op == "s_nop":
-                ws += int(u.split()[1], 0) + 1
-                continue
-            ws += 1
-            if op.startswith("v_mfma"):
-                continue
-            reads, writes = _accesses(u)
-            if reads & dst:
-                found.append(f"{kernel}: '{u}' reads the result of '{t}' after {ws} wait states")
-            elif writes & dst:
-                found.append(f"{kernel}: '{u}' overwrites the result of '{t}' after {ws} wait states")
+        walk_back(i, srcs, t, kernel, found)
+        walk_forward(i + 1, dst, t, kernel, found)
     return found
 
 

@@ -114,3 +114,24 @@ def test_built_forward_kernels_use_no_scratch():
     sizes = private_segment_sizes(text)
     assert any("Bf16DmaILi128" in k for k in sizes)  # the D = 128 forward kernels are in the build
     assert scratch_findings(text) == []
+
+
+def test_a_block_the_common_path_branches_over_is_no_distance():
+    # the read after the label is reached by the branch after two instructions, not 40
+    asm = _asm("s_nop 7", "s_cbranch_scc1 .LBB0_2", *(["v_add_f32 v1, v2, v3"] * 40), ".LBB0_2:",
+               "v_mov_b32 v40, v12")
+    assert len(inline_mfma_hazards(asm)) == 1
+    # a jump skips the instructions after it as well
+    asm = _asm("s_branch .LBB0_3", *(["v_add_f32 v1, v2, v3"] * 40), ".LBB0_3:", "v_mov_b32 v40, v12")
+    assert len(inline_mfma_hazards(asm)) == 1
+    # enough distance on the branch path too: clean
+    asm = _asm("s_nop 7", "s_nop 7", "s_nop 7", "s_cbranch_scc1 .LBB0_4", "v_add_f32 v1, v2, v3", ".LBB0_4:",
+               "v_mov_b32 v40, v12")
+    assert inline_mfma_hazards(asm) == []
+
+
+def test_an_operand_written_at_the_end_of_a_loop_is_found():
+    # the loop's back edge brings the VALU write right before the MFMA at the loop head
+    asm = "\n".join(["_Zk:", "s_mov_b32 s0, 0", ".LBB0_1:", ";;#ASMSTART", AGPR_MFMA, ";;#ASMEND",
+                     *(["v_add_f32 v1, v2, v3"] * 30), "v_cvt_pk_bf16_f32 v7, v40, v41", "s_cbranch_scc1 .LBB0_1"])
+    assert len(inline_mfma_hazards(asm)) == 1
